@@ -1,0 +1,205 @@
+#!/usr/bin/env python3
+"""Ring-fold attention throughput on one MI355X.
+
+One step = one ra_ring_forward over the whole workload: all P virtual ring
+steps (fold launches plus the double-buffered K/V hand-off) for every resident
+query block, including the final normalisation.  Inputs are resident in HBM
+before timing starts.  Prints ONE JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
+                    [--no-cpu-baseline] [--cpu-seconds S]
+
+The default workload is the 128K-token ring (B1 H32 d128 N131072 P16, all 16
+query blocks resident).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "ring-fold attention TFLOP/s and % MFMA bf16 peak, 128K tokens P=16, 1 GPU"
+PEAK = {"bf16": 2500.0, "f32": 157.3}  # MI355X published dense TFLOP/s: bf16 MFMA, fp32 vector
+FOLD_SOURCES = {"bf16": "fold_bf16.hip", "f32": "fold_f32.hip"}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fold_traffic.json")
+
+
+def _source_hash(dtype: str) -> str:
+    path = os.path.join(ROOT, "blockwise_online_softmax_fold_amd", "csrc", FOLD_SOURCES[dtype])
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _traffic(workload: str, dtype: str):
+    """HBM bytes per fold launch from the committed rocprofv3 counter summary,
+    only if it was taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get(workload)
+    if not ent or ent.get("source_sha256_16") != _source_hash(dtype):
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def _blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+
+        n = [i["num_threads"] for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(w, q, k, v, seconds: float) -> dict:
+    """Time the fp64 oracle (as it stands) on a bounded sample of the same
+    workload: whole query rows against all N keys of one head, in chunks, until
+    about ``seconds`` of CPU work.  Rate in the metric's unit (TFLOP/s)."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    k64 = k[0, 0].to("cpu", torch.float64).numpy()
+    v64 = v[0, 0].to("cpu", torch.float64).numpy()
+    q64 = q[0, 0].to("cpu", torch.float64).numpy()
+    chunk = 256
+    rows_done, elapsed, r0 = 0, 0.0, 0
+    while elapsed < seconds and rows_done < q64.shape[0]:
+        qs = q64[r0:r0 + chunk]
+        t0 = time.perf_counter()
+        oracle.dense_attention(qs, k64, v64)
+        elapsed += time.perf_counter() - t0
+        rows_done += qs.shape[0]
+        r0 = (r0 + chunk) % q64.shape[0]
+    flops = 4.0 * rows_done * w.N * w.d
+    del np
+    return {
+        "value": flops / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": _blas_threads(),
+        "kind": "oracle",
+        "sample": f"fp64 dense oracle, {rows_done} query rows x {w.N} keys x d={w.d} of head 0 "
+                  f"({elapsed:.1f} s; full workload is {w.B * w.H * w.n_q * w.b} rows)",
+        "host_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the ring's P devices run as virtual steps on a single MI355X, "
+              "so --gpus must be 1 (no multi-GPU path is built).", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import blockwise_online_softmax_fold_amd as ra
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+    ra.load()
+    w = workloads.WORKLOADS[args.workload]
+    print(f"[bench] workload {w.describe()} steps={args.steps} warmup={args.warmup}", file=sys.stderr, flush=True)
+    q, k, v = workloads.make_inputs(w, device="cuda")
+    out = torch.empty_like(q)
+    ws = torch.empty(ra.ra_ring_workspace_bytes(q.dtype, w.B, w.H, w.N, w.d, w.P, w.n_q), dtype=torch.uint8,
+                     device="cuda")
+    qb = w.query_blocks
+
+    def step():
+        ra.ra_ring_forward(q, k, v, w.P, query_blocks=qb, out=out, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print("[bench] warmup done", file=sys.stderr, flush=True)
+
+    ra.ra_profile_folds(True)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    launches, fold_ms_total, fold_ms_max = ra.ra_profile_read()
+    ra.ra_profile_folds(False)
+    print(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
+
+    flops = w.flops()
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = PEAK[w.dtype]
+    launches_per_step = launches / args.steps
+    fold_avg_ms = fold_ms_total / launches
+    flops_per_launch = flops / launches_per_step
+    achieved = flops_per_launch / (fold_avg_ms * 1e-3) / 1e12
+    roofline = {
+        "bound": "mfma" if w.dtype == "bf16" else "alu",
+        "achieved": round(achieved, 2),
+        "peak": peak,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / peak, 4),
+        "traffic": _traffic(w.name, w.dtype),
+        "kernel": f"fold_{w.dtype}_kernel<{w.d}>",
+        "flop_per_launch": flops_per_launch,
+        "avg_launch_ms": round(fold_avg_ms, 4),
+        "max_launch_ms": round(fold_ms_max, 4),
+        "launches": launches,
+    }
+    rec = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "P": w.P, "b": w.b,
+                   "resident_query_blocks": w.n_q, "seed": w.seed, "causal": False},
+        "pct_mfma_peak": round(100.0 * tflops / peak, 2),
+        "exps_per_s": w.exps() / (ms * 1e-3),
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        print(f"[bench] timing the CPU oracle for ~{args.cpu_seconds:.0f} s", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

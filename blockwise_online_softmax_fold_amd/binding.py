@@ -1,0 +1,229 @@
+"""ctypes binding of libra.so (include/ra.h), with the same entry-point names.
+
+This layer only marshals arguments: torch tensors become device pointers and
+element strides, the current torch stream becomes the hipStream_t.  Every step
+of the computation runs in the library's HIP kernels.  If the library is not
+built, every call raises; nothing falls back to another implementation.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Sequence
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libra.so")
+_lib = None
+
+RA_OK = 0
+RA_E_INVALID_ARG = 1
+RA_E_UNSUPPORTED = 2
+RA_E_HIP = 3
+RA_E_OOM = 4
+RA_DTYPE_F32 = 0
+RA_DTYPE_BF16 = 1
+
+#: every symbol include/ra.h declares
+EXPORTED = (
+    "ra_state_init",
+    "ra_fold_block",
+    "ra_finalize",
+    "ra_ring_workspace_bytes",
+    "ra_ring_forward",
+    "ra_last_error",
+    "ra_version",
+    "ra_profile_folds",
+    "ra_profile_read",
+)
+
+_STATUS_NAMES = {0: "RA_OK", 1: "RA_E_INVALID_ARG", 2: "RA_E_UNSUPPORTED", 3: "RA_E_HIP", 4: "RA_E_OOM"}
+
+
+class RaError(RuntimeError):
+    """A non-zero ra_status_t; ``status`` holds the code, the message ra_last_error()."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load() -> ctypes.CDLL:
+    """Load libra.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is missing: build it with `python -m blockwise_online_softmax_fold_amd.build` "
+            "(or __graft_entry__.build()); there is no fallback implementation"
+        )
+    lib = ctypes.CDLL(_LIB_PATH)
+    i64, i32, f32, vp, sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+    strides = ctypes.POINTER(ctypes.c_int64)
+    lib.ra_state_init.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp]
+    lib.ra_state_init.restype = ctypes.c_int
+    lib.ra_fold_block.argtypes = [vp, strides, vp, strides, vp, strides, ctypes.c_int, i64, i64, i64, i64, i64, f32,
+                                  vp, vp, vp, vp]
+    lib.ra_fold_block.restype = ctypes.c_int
+    lib.ra_finalize.argtypes = [vp, vp, vp, strides, ctypes.c_int, i64, i64, i64, i64, vp]
+    lib.ra_finalize.restype = ctypes.c_int
+    lib.ra_ring_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i64, i64, i32, i32]
+    lib.ra_ring_workspace_bytes.restype = sz
+    lib.ra_ring_forward.argtypes = [vp, strides, vp, strides, vp, strides, vp, strides, ctypes.c_int, i64, i64, i64,
+                                    i64, i32, ctypes.POINTER(ctypes.c_int32), i32, f32, vp, sz, vp]
+    lib.ra_ring_forward.restype = ctypes.c_int
+    lib.ra_last_error.argtypes = []
+    lib.ra_last_error.restype = ctypes.c_char_p
+    lib.ra_version.argtypes = []
+    lib.ra_version.restype = ctypes.c_char_p
+    lib.ra_profile_folds.argtypes = [ctypes.c_int]
+    lib.ra_profile_folds.restype = ctypes.c_int
+    lib.ra_profile_read.argtypes = [ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
+    lib.ra_profile_read.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def ra_last_error() -> str:
+    return load().ra_last_error().decode()
+
+
+def ra_version() -> str:
+    return load().ra_version().decode()
+
+
+def _check(status: int) -> None:
+    if status != RA_OK:
+        raise RaError(status, ra_last_error())
+
+
+# ---------------------------------------------------------------------------
+# torch marshalling helpers
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return RA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return RA_DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: use torch.bfloat16 or torch.float32")
+
+
+def _strides(t):
+    """Element strides {batch, head, row} of a [B, H, rows, d] tensor."""
+    if t.dim() != 4:
+        raise ValueError(f"expected a [B, H, rows, d] tensor, got shape {tuple(t.shape)}")
+    if t.shape[-1] > 1 and t.stride(-1) != 1:
+        raise ValueError("the last (d) axis must be contiguous")
+    return (ctypes.c_int64 * 3)(t.stride(0), t.stride(1), t.stride(2))
+
+
+def _dev(t, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _state_ok(m, l, o):
+    import torch
+
+    for name, t in (("m", m), ("l", l), ("o", o)):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError(f"state {name} must be a contiguous float32 tensor")
+
+
+# ---------------------------------------------------------------------------
+# entry points
+
+
+def ra_state_init(m, l, o, stream=None) -> None:
+    """(m, l, o) = (-inf, 0, 0).  m, l: [B, H, rows]; o: [B, H, rows, d]."""
+    _state_ok(m, l, o)
+    B, H, rows, d = o.shape
+    _check(load().ra_state_init(_dev(m, "m"), _dev(l, "l"), _dev(o, "o"), B, H, rows, d, _stream(stream)))
+
+
+def ra_fold_block(q, k, v, m, l, o, scale: float = 0.0, stream=None) -> None:
+    """Fold one visiting block (k, v: [B, H, kv_rows, d]) into the state of q's rows."""
+    _state_ok(m, l, o)
+    B, H, q_rows, d = q.shape
+    kv_rows = k.shape[2]
+    if k.shape != v.shape or k.shape[:2] != q.shape[:2] or k.shape[3] != d:
+        raise ValueError(f"shapes q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)} do not match")
+    if tuple(o.shape) != (B, H, q_rows, d) or tuple(m.shape) != (B, H, q_rows) or tuple(l.shape) != (B, H, q_rows):
+        raise ValueError("state shapes do not match q")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must have one dtype")
+    _check(load().ra_fold_block(
+        _dev(q, "q"), _strides(q), _dev(k, "k"), _strides(k), _dev(v, "v"), _strides(v), _dtype_code(q),
+        B, H, q_rows, kv_rows, d, float(scale), _dev(m, "m"), _dev(l, "l"), _dev(o, "o"), _stream(stream)))
+
+
+def ra_finalize(l, o, out, stream=None) -> None:
+    """out = o / l (0 where l == 0), cast to out's dtype."""
+    B, H, rows, d = o.shape
+    _check(load().ra_finalize(_dev(l, "l"), _dev(o, "o"), _dev(out, "out"), _strides(out), _dtype_code(out),
+                              B, H, rows, d, _stream(stream)))
+
+
+def ra_ring_workspace_bytes(dtype, B: int, H: int, N: int, d: int, P: int, n_q: int) -> int:
+    import torch
+
+    code = RA_DTYPE_BF16 if dtype == torch.bfloat16 else RA_DTYPE_F32 if dtype == torch.float32 else -1
+    return int(load().ra_ring_workspace_bytes(code, B, H, N, d, P, n_q))
+
+
+def ra_ring_forward(q, k, v, P: int, query_blocks: Sequence[int] | None = None, out=None, scale: float = 0.0,
+                    workspace=None, stream=None):
+    """The whole ring for the resident query blocks; returns out ([B, H, n_q*b, d])."""
+    import torch
+
+    B, H, N, d = k.shape
+    if v.shape != k.shape:
+        raise ValueError("k and v must have the same shape")
+    n_q = P if query_blocks is None else len(query_blocks)
+    if P >= 1 and N % P == 0 and (q.shape[:2] != k.shape[:2] or q.shape[3] != d or q.shape[2] != n_q * (N // P)):
+        raise ValueError(f"q must be [B, H, n_q*N/P, d] = [{B}, {H}, {n_q * (N // P)}, {d}], got {tuple(q.shape)}")
+    if out is not None and out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    if out is None:
+        out = torch.empty_like(q)
+    qb = None
+    if query_blocks is not None:
+        qb = (ctypes.c_int32 * max(1, n_q))(*[int(x) for x in query_blocks])
+    ws_ptr, ws_bytes = ctypes.c_void_p(None), 0
+    if workspace is not None:
+        ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+    if not (q.dtype == k.dtype == v.dtype == out.dtype):
+        raise TypeError("q, k, v and out must have one dtype")
+    _check(load().ra_ring_forward(
+        _dev(q, "q"), _strides(q), _dev(k, "k"), _strides(k), _dev(v, "v"), _strides(v), _dev(out, "out"),
+        _strides(out), _dtype_code(q), B, H, N, d, int(P), qb, n_q, float(scale), ws_ptr, ws_bytes,
+        _stream(stream)))
+    return out
+
+
+def ra_profile_folds(enable: bool) -> None:
+    """Time every fold launch of ra_ring_forward with HIP events on its stream."""
+    _check(load().ra_profile_folds(1 if enable else 0))
+
+
+def ra_profile_read():
+    """(launches, total_ms, max_ms) of the fold launches timed since the last read."""
+    n, tot, mx = ctypes.c_int64(), ctypes.c_double(), ctypes.c_double()
+    _check(load().ra_profile_read(ctypes.byref(n), ctypes.byref(tot), ctypes.byref(mx)))
+    return int(n.value), float(tot.value), float(mx.value)

@@ -1,0 +1,488 @@
+// Host side of libra.so: argument checks, workspace layout, the ring driver
+// (P virtual ring steps with a double-buffered K/V hand-off on a side stream)
+// and the C entry points declared in include/ra.h.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "ra.h"
+
+#define RA_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+using ra::FoldParams;
+
+thread_local std::string g_err;
+
+ra_status_t fail(ra_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+ra_status_t hip_fail(hipError_t e, const char* what) {
+  g_err = std::string(what) + ": " + hipGetErrorString(e);
+  return e == hipErrorOutOfMemory ? RA_E_OOM : RA_E_HIP;
+}
+
+#define RA_HIP(call, what)                \
+  do {                                    \
+    hipError_t e_ = (call);               \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+
+bool valid_d(int64_t d) { return d == 64 || d == 128 || d == 256; }
+bool valid_dt(ra_dtype_t dt) { return dt == RA_DTYPE_F32 || dt == RA_DTYPE_BF16; }
+size_t esize(ra_dtype_t dt) { return dt == RA_DTYPE_BF16 ? 2 : 4; }
+
+ra_status_t check_tensor(const char* name, const void* ptr, const int64_t* strides, ra_dtype_t dt) {
+  if (ptr == nullptr) return fail(RA_E_INVALID_ARG, "%s is NULL", name);
+  if (strides == nullptr) return fail(RA_E_INVALID_ARG, "%s strides are NULL", name);
+  if (((uintptr_t)ptr & 15) != 0) return fail(RA_E_INVALID_ARG, "%s is not 16-byte aligned", name);
+  const int64_t q = dt == RA_DTYPE_BF16 ? 8 : 4;
+  for (int i = 0; i < 3; ++i) {
+    if (strides[i] < 0) return fail(RA_E_INVALID_ARG, "%s stride %d is negative", name, i);
+    if (strides[i] % q != 0)
+      return fail(RA_E_INVALID_ARG, "%s stride %d (%lld) is not a multiple of %lld elements", name, i,
+                  (long long)strides[i], (long long)q);
+  }
+  return RA_OK;
+}
+
+ra_status_t check_state(const float* m, const float* l, const float* o) {
+  if (!m || !l || !o) return fail(RA_E_INVALID_ARG, "state pointer m, l or o is NULL");
+  if (((uintptr_t)o & 15) != 0) return fail(RA_E_INVALID_ARG, "state o is not 16-byte aligned");
+  if (((uintptr_t)m & 3) != 0 || ((uintptr_t)l & 3) != 0)
+    return fail(RA_E_INVALID_ARG, "state m or l is not 4-byte aligned");
+  return RA_OK;
+}
+
+ra_status_t check_common(ra_dtype_t dt, int64_t B, int64_t H, int64_t d) {
+  if (!valid_dt(dt)) return fail(RA_E_INVALID_ARG, "unknown dtype %d", (int)dt);
+  if (B < 1 || H < 1) return fail(RA_E_INVALID_ARG, "B=%lld and H=%lld must be >= 1", (long long)B, (long long)H);
+  if (B > 65535 || H > 65535) return fail(RA_E_UNSUPPORTED, "B and H must be <= 65535");
+  if (!valid_d(d)) return fail(RA_E_UNSUPPORTED, "head dim d=%lld is not 64, 128 or 256", (long long)d);
+  return RA_OK;
+}
+
+ra_status_t resolve_scale(float scale, int64_t d, float* out) {
+  if (scale == 0.0f) {
+    *out = (float)(1.0 / sqrt((double)d));
+    return RA_OK;
+  }
+  if (!(scale > 0.0f) || !isfinite(scale))
+    return fail(RA_E_INVALID_ARG, "scale must be 0 (meaning 1/sqrt(d)) or finite and > 0");
+  *out = scale;
+  return RA_OK;
+}
+
+float to_log2_scale(float scale) { return (float)((double)scale * 1.4426950408889634); }
+
+// Per-device resources owned by the library: the side stream of the hand-off
+// and the events ordering it against the caller's stream.
+struct DevRes {
+  hipStream_t side = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  hipEvent_t ready[2] = {nullptr, nullptr};
+  hipEvent_t freed[2] = {nullptr, nullptr};
+  std::mutex mu;  // one ring driver at a time per device uses these
+};
+
+std::mutex g_dev_mu;
+std::map<int, DevRes*> g_dev;
+
+ra_status_t get_dev(DevRes** out) {
+  int dev = 0;
+  RA_HIP(hipGetDevice(&dev), "hipGetDevice");
+  std::lock_guard<std::mutex> g(g_dev_mu);
+  auto it = g_dev.find(dev);
+  if (it != g_dev.end()) {
+    *out = it->second;
+    return RA_OK;
+  }
+  DevRes* r = new DevRes;
+  RA_HIP(hipStreamCreateWithFlags(&r->side, hipStreamNonBlocking), "hipStreamCreateWithFlags");
+  hipEvent_t* evs[6] = {&r->fork, &r->join, &r->ready[0], &r->ready[1], &r->freed[0], &r->freed[1]};
+  for (hipEvent_t* e : evs) RA_HIP(hipEventCreateWithFlags(e, hipEventDisableTiming), "hipEventCreateWithFlags");
+  g_dev[dev] = r;
+  *out = r;
+  return RA_OK;
+}
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Workspace of the ring driver: state of the n_q resident blocks
+// (m, l: [B, H, n_q*b]; o: [B, H, n_q*b, d]) followed by the K and V halves
+// of the double buffer, each [slot][n_q][B][H][b][d].
+struct RingLayout {
+  int64_t b = 0, rows = 0;
+  int nslots = 0;
+  size_t off_m = 0, off_l = 0, off_o = 0, off_k = 0, off_v = 0, total = 0;
+  int64_t res_elems = 0;   // K (or V) elements of one resident block's slot
+  int64_t slot_elems = 0;  // elements of one slot over all residents
+};
+
+RingLayout ring_layout(ra_dtype_t dt, int64_t B, int64_t H, int64_t N, int64_t d, int32_t P, int32_t n_q) {
+  RingLayout L;
+  L.b = N / P;
+  L.rows = (int64_t)n_q * L.b;
+  L.nslots = P - 1 < 2 ? P - 1 : 2;  // two visiting blocks, not P
+  const size_t st_rows = (size_t)B * H * L.rows;
+  L.off_m = 0;
+  L.off_l = round_up(L.off_m + st_rows * 4);
+  L.off_o = round_up(L.off_l + st_rows * 4);
+  L.off_k = round_up(L.off_o + st_rows * (size_t)d * 4);
+  L.res_elems = B * H * L.b * d;
+  L.slot_elems = L.res_elems * n_q;
+  const size_t buf = (size_t)L.nslots * L.slot_elems * esize(dt);
+  L.off_v = round_up(L.off_k + buf);
+  L.total = round_up(L.off_v + buf);
+  return L;
+}
+
+ra_status_t check_ring(const void* q, const int64_t* q_strides, const void* k, const int64_t* k_strides,
+                       const void* v, const int64_t* v_strides, const void* out, const int64_t* out_strides,
+                       ra_dtype_t dt, int64_t B, int64_t H, int64_t N, int64_t d, int32_t P,
+                       const int32_t* query_blocks, int32_t n_q) {
+  ra_status_t st = check_common(dt, B, H, d);
+  if (st != RA_OK) return st;
+  if (P < 1) return fail(RA_E_INVALID_ARG, "P=%d must be >= 1", (int)P);
+  if (N < P) return fail(RA_E_INVALID_ARG, "N=%lld must be >= P=%d", (long long)N, (int)P);
+  if (N % P != 0) return fail(RA_E_UNSUPPORTED, "N=%lld is not a multiple of P=%d", (long long)N, (int)P);
+  if (N / P > 0x7fffffffLL / 4) return fail(RA_E_UNSUPPORTED, "block size N/P is too large");
+  if (n_q < 1) return fail(RA_E_INVALID_ARG, "n_q=%d must be >= 1", (int)n_q);
+  if (query_blocks == nullptr && n_q != P)
+    return fail(RA_E_INVALID_ARG, "query_blocks is NULL (all blocks) but n_q=%d != P=%d", (int)n_q, (int)P);
+  if (query_blocks != nullptr)
+    for (int32_t i = 0; i < n_q; ++i)
+      if (query_blocks[i] < 0 || query_blocks[i] >= P)
+        return fail(RA_E_INVALID_ARG, "query_blocks[%d]=%d is outside [0, P=%d)", (int)i, (int)query_blocks[i],
+                    (int)P);
+  if ((st = check_tensor("q", q, q_strides, dt)) != RA_OK) return st;
+  if ((st = check_tensor("k", k, k_strides, dt)) != RA_OK) return st;
+  if ((st = check_tensor("v", v, v_strides, dt)) != RA_OK) return st;
+  if ((st = check_tensor("out", out, out_strides, dt)) != RA_OK) return st;
+  return RA_OK;
+}
+
+void set_strides(int64_t* dst_b, int64_t* dst_h, int64_t* dst_r, const int64_t* s) {
+  *dst_b = s[0];
+  *dst_h = s[1];
+  *dst_r = s[2];
+}
+
+// Copy block j of src ([B, H, N, d] with strides s) into a contiguous
+// [B, H, b, d] region at dst (the hand-off of one visiting block).
+ra_status_t copy_block(void* dst, const void* src, const int64_t* s, int64_t B, int64_t H, int64_t b, int64_t d,
+                       int64_t j, size_t es, hipStream_t stream) {
+  const char* sp = (const char*)src;
+  char* dp = (char*)dst;
+  const size_t row_bytes = (size_t)d * es;
+  const size_t blk_bytes = (size_t)b * row_bytes;
+  if (s[2] == d && (H == 1 || s[1] * (int64_t)es >= (int64_t)blk_bytes)) {
+    // rows of a block are contiguous: one 2-D copy over heads per batch
+    const size_t spitch = H == 1 ? blk_bytes : (size_t)s[1] * es;
+    for (int64_t bi = 0; bi < B; ++bi) {
+      const char* from = sp + (size_t)(bi * s[0] + j * b * d) * es;
+      char* to = dp + (size_t)bi * H * blk_bytes;
+      RA_HIP(hipMemcpy2DAsync(to, blk_bytes, from, spitch, blk_bytes, (size_t)H, hipMemcpyDeviceToDevice, stream),
+             "hipMemcpy2DAsync (hand-off)");
+    }
+    return RA_OK;
+  }
+  for (int64_t bi = 0; bi < B; ++bi)
+    for (int64_t hi = 0; hi < H; ++hi) {
+      const char* from = sp + (size_t)(bi * s[0] + hi * s[1] + j * b * s[2]) * es;
+      char* to = dp + (size_t)(bi * H + hi) * blk_bytes;
+      RA_HIP(hipMemcpy2DAsync(to, row_bytes, from, (size_t)s[2] * es, row_bytes, (size_t)b, hipMemcpyDeviceToDevice,
+                              stream),
+             "hipMemcpy2DAsync (hand-off)");
+    }
+  return RA_OK;
+}
+
+hipError_t launch_fold(const FoldParams& p, ra_dtype_t dt, int d, hipStream_t s) {
+  return dt == RA_DTYPE_BF16 ? ra::launch_fold_bf16(p, d, s) : ra::launch_fold_f32(p, d, s);
+}
+
+// Optional per-launch timing of the fold kernels (ra_profile_folds).
+struct FoldProfile {
+  std::mutex mu;
+  bool on = false;
+  std::vector<hipEvent_t> ev;  // pairs: start, stop
+  size_t used = 0;             // pairs recorded
+};
+FoldProfile g_prof;
+constexpr size_t kMaxProfiled = 4096;
+
+// Record the start event of a timed launch; returns the pair index or -1.
+long prof_begin(hipStream_t s) {
+  std::lock_guard<std::mutex> g(g_prof.mu);
+  if (!g_prof.on || g_prof.used >= kMaxProfiled) return -1;
+  const size_t i = g_prof.used;
+  while (g_prof.ev.size() < 2 * (i + 1)) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return -1;
+    g_prof.ev.push_back(e);
+  }
+  if (hipEventRecord(g_prof.ev[2 * i], s) != hipSuccess) return -1;
+  g_prof.used = i + 1;
+  return (long)i;
+}
+
+void prof_end(long i, hipStream_t s) {
+  if (i < 0) return;
+  std::lock_guard<std::mutex> g(g_prof.mu);
+  (void)hipEventRecord(g_prof.ev[2 * i + 1], s);
+}
+
+bool env_flag(const char* name) {
+  const char* v = getenv(name);
+  return v != nullptr && v[0] != '\0' && v[0] != '0';
+}
+
+}  // namespace
+
+RA_API const char* ra_last_error(void) { return g_err.c_str(); }
+
+RA_API const char* ra_version(void) { return "0.1.0"; }
+
+RA_API ra_status_t ra_state_init(float* m, float* l, float* o, int64_t B, int64_t H, int64_t rows, int64_t d,
+                                 void* stream) {
+  g_err.clear();
+  ra_status_t st = check_common(RA_DTYPE_F32, B, H, d);
+  if (st != RA_OK) return st;
+  if (rows < 0) return fail(RA_E_INVALID_ARG, "rows=%lld must be >= 0", (long long)rows);
+  if ((st = check_state(m, l, o)) != RA_OK) return st;
+  if (rows == 0) return RA_OK;
+  RA_HIP(ra::launch_state_init(m, l, o, B * H * rows, (int)d, (hipStream_t)stream), "state init launch");
+  return RA_OK;
+}
+
+RA_API ra_status_t ra_fold_block(const void* q, const int64_t q_strides[3], const void* k, const int64_t k_strides[3],
+                                 const void* v, const int64_t v_strides[3], ra_dtype_t dt, int64_t B, int64_t H,
+                                 int64_t q_rows, int64_t kv_rows, int64_t d, float scale, float* m, float* l,
+                                 float* o, void* stream) {
+  g_err.clear();
+  ra_status_t st = check_common(dt, B, H, d);
+  if (st != RA_OK) return st;
+  if (q_rows < 0 || kv_rows < 0) return fail(RA_E_INVALID_ARG, "q_rows and kv_rows must be >= 0");
+  if (q_rows > 0x7fffffffLL / 4 || kv_rows > 0x7fffffffLL / 4)
+    return fail(RA_E_UNSUPPORTED, "q_rows or kv_rows is too large for one launch");
+  float sc;
+  if ((st = resolve_scale(scale, d, &sc)) != RA_OK) return st;
+  if ((st = check_tensor("q", q, q_strides, dt)) != RA_OK) return st;
+  if ((st = check_tensor("k", k, k_strides, dt)) != RA_OK) return st;
+  if ((st = check_tensor("v", v, v_strides, dt)) != RA_OK) return st;
+  if ((st = check_state(m, l, o)) != RA_OK) return st;
+  if (q_rows == 0 || kv_rows == 0) return RA_OK;  // nothing to fold
+
+  FoldParams p = {};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.out = nullptr;
+  p.m = m;
+  p.l = l;
+  p.o = o;
+  set_strides(&p.q_sb, &p.q_sh, &p.q_sr, q_strides);
+  set_strides(&p.k_sb, &p.k_sh, &p.k_sr, k_strides);
+  set_strides(&p.v_sb, &p.v_sh, &p.v_sr, v_strides);
+  p.st_bh = q_rows;
+  p.k_off[0] = 0;
+  p.v_off[0] = 0;
+  p.B = (int32_t)B;
+  p.H = (int32_t)H;
+  p.n_res = 1;
+  p.q_rows = (int32_t)q_rows;
+  p.kv_rows = (int32_t)kv_rows;
+  p.flags = ra::kLoadState | ra::kStoreState;
+  p.scale_log2 = to_log2_scale(sc);
+  RA_HIP(launch_fold(p, dt, (int)d, (hipStream_t)stream), "fold launch");
+  return RA_OK;
+}
+
+RA_API ra_status_t ra_finalize(const float* l, const float* o, void* out, const int64_t out_strides[3],
+                               ra_dtype_t out_dt, int64_t B, int64_t H, int64_t rows, int64_t d, void* stream) {
+  g_err.clear();
+  ra_status_t st = check_common(out_dt, B, H, d);
+  if (st != RA_OK) return st;
+  if (rows < 0) return fail(RA_E_INVALID_ARG, "rows=%lld must be >= 0", (long long)rows);
+  if (l == nullptr || o == nullptr) return fail(RA_E_INVALID_ARG, "state pointer l or o is NULL");
+  if (((uintptr_t)o & 15) != 0) return fail(RA_E_INVALID_ARG, "state o is not 16-byte aligned");
+  if ((st = check_tensor("out", out, out_strides, out_dt)) != RA_OK) return st;
+  if (rows == 0) return RA_OK;
+  RA_HIP(ra::launch_finalize(l, o, out, out_dt == RA_DTYPE_BF16, out_strides[0], out_strides[1], out_strides[2],
+                             (int)B, (int)H, rows, (int)d, (hipStream_t)stream),
+         "finalize launch");
+  return RA_OK;
+}
+
+RA_API size_t ra_ring_workspace_bytes(ra_dtype_t dt, int64_t B, int64_t H, int64_t N, int64_t d, int32_t P,
+                                      int32_t n_q) {
+  const std::string saved = g_err;
+  const bool ok = check_common(dt, B, H, d) == RA_OK && P >= 1 && N >= P && N % P == 0 && n_q >= 1 &&
+                  N / P <= 0x7fffffffLL / 4;
+  g_err = saved;
+  if (!ok) return 0;
+  return ring_layout(dt, B, H, N, d, P, n_q).total;
+}
+
+RA_API ra_status_t ra_ring_forward(const void* q, const int64_t q_strides[3], const void* k,
+                                   const int64_t k_strides[3], const void* v, const int64_t v_strides[3], void* out,
+                                   const int64_t out_strides[3], ra_dtype_t dt, int64_t B, int64_t H, int64_t N,
+                                   int64_t d, int32_t P, const int32_t* query_blocks, int32_t n_q, float scale,
+                                   void* workspace, size_t workspace_bytes, void* stream_) {
+  g_err.clear();
+  ra_status_t st = check_ring(q, q_strides, k, k_strides, v, v_strides, out, out_strides, dt, B, H, N, d, P,
+                              query_blocks, n_q);
+  if (st != RA_OK) return st;
+  float sc;
+  if ((st = resolve_scale(scale, d, &sc)) != RA_OK) return st;
+  const RingLayout L = ring_layout(dt, B, H, N, d, P, n_q);
+  if (workspace != nullptr) {
+    if (workspace_bytes < L.total)
+      return fail(RA_E_INVALID_ARG, "workspace of %zu bytes is smaller than the %zu bytes needed", workspace_bytes,
+                  L.total);
+    if (((uintptr_t)workspace & (kAlign - 1)) != 0)
+      return fail(RA_E_INVALID_ARG, "workspace is not %zu-byte aligned", kAlign);
+  }
+  auto qb = [&](int32_t r) { return query_blocks ? query_blocks[r] : r; };
+
+  hipStream_t stream = (hipStream_t)stream_;
+  DevRes* dr = nullptr;
+  if ((st = get_dev(&dr)) != RA_OK) return st;
+  std::lock_guard<std::mutex> guard(dr->mu);
+
+  void* ws = workspace;
+  const bool own_ws = ws == nullptr;
+  if (own_ws) RA_HIP(hipMallocAsync(&ws, L.total, stream), "hipMallocAsync (ring workspace)");
+  char* base = (char*)ws;
+  float* m = (float*)(base + L.off_m);
+  float* l = (float*)(base + L.off_l);
+  float* o = (float*)(base + L.off_o);
+  char* kbuf = base + L.off_k;
+  char* vbuf = base + L.off_v;
+  const size_t es = esize(dt);
+  const int64_t b = L.b;
+
+  const bool serial = env_flag("RA_SYNC_EACH_STEP");
+  hipStream_t side = serial ? stream : dr->side;
+  if (!serial) {
+    RA_HIP(hipEventRecord(dr->fork, stream), "hipEventRecord");
+    RA_HIP(hipStreamWaitEvent(side, dr->fork, 0), "hipStreamWaitEvent");
+  }
+  // Data for step t >= 1 lives in slot (t - 1) % 2.
+  auto slot_of = [](int t) { return (t - 1) & 1; };
+
+  for (int t = 0; t < P; ++t) {
+    if (t + 1 < P) {
+      // Hand-off for step t + 1 (the "send to i+1 / receive from i-1" of
+      // step t), issued before step t's fold so the two overlap.
+      const int s = slot_of(t + 1);
+      if (!serial && t + 1 >= 3) RA_HIP(hipStreamWaitEvent(side, dr->freed[s], 0), "hipStreamWaitEvent");
+      for (int32_t r = 0; r < n_q; ++r) {
+        const int64_t j = ((int64_t)qb(r) - (t + 1)) % P;
+        const int64_t jj = j < 0 ? j + P : j;
+        char* kd = kbuf + ((size_t)s * L.slot_elems + (size_t)r * L.res_elems) * es;
+        char* vd = vbuf + ((size_t)s * L.slot_elems + (size_t)r * L.res_elems) * es;
+        if ((st = copy_block(kd, k, k_strides, B, H, b, d, jj, es, side)) != RA_OK) return st;
+        if ((st = copy_block(vd, v, v_strides, B, H, b, d, jj, es, side)) != RA_OK) return st;
+      }
+      if (!serial) RA_HIP(hipEventRecord(dr->ready[s], side), "hipEventRecord");
+    }
+    if (t >= 1 && !serial) RA_HIP(hipStreamWaitEvent(stream, dr->ready[slot_of(t)], 0), "hipStreamWaitEvent");
+
+    for (int32_t r0 = 0; r0 < n_q; r0 += ra::kMaxResident) {
+      const int32_t nr = n_q - r0 < ra::kMaxResident ? n_q - r0 : ra::kMaxResident;
+      FoldParams p = {};
+      p.q = (const char*)q + (size_t)r0 * b * q_strides[2] * es;
+      p.out = (char*)out + (size_t)r0 * b * out_strides[2] * es;
+      p.m = m + (size_t)r0 * b;
+      p.l = l + (size_t)r0 * b;
+      p.o = o + (size_t)r0 * b * d;
+      set_strides(&p.q_sb, &p.q_sh, &p.q_sr, q_strides);
+      set_strides(&p.out_sb, &p.out_sh, &p.out_sr, out_strides);
+      p.st_bh = L.rows;
+      if (t == 0) {  // the own block, read in place
+        p.k = k;
+        p.v = v;
+        set_strides(&p.k_sb, &p.k_sh, &p.k_sr, k_strides);
+        set_strides(&p.v_sb, &p.v_sh, &p.v_sr, v_strides);
+        for (int32_t r = 0; r < nr; ++r) {
+          p.k_off[r] = (int64_t)qb(r0 + r) * b * k_strides[2];
+          p.v_off[r] = (int64_t)qb(r0 + r) * b * v_strides[2];
+        }
+      } else {
+        const int s = slot_of(t);
+        p.k = kbuf + (size_t)s * L.slot_elems * es;
+        p.v = vbuf + (size_t)s * L.slot_elems * es;
+        p.k_sb = p.v_sb = H * b * d;
+        p.k_sh = p.v_sh = b * d;
+        p.k_sr = p.v_sr = d;
+        for (int32_t r = 0; r < nr; ++r) p.k_off[r] = p.v_off[r] = (int64_t)(r0 + r) * L.res_elems;
+      }
+      p.B = (int32_t)B;
+      p.H = (int32_t)H;
+      p.n_res = nr;
+      p.q_rows = (int32_t)b;
+      p.kv_rows = (int32_t)b;
+      p.flags = (t == 0 ? 0 : ra::kLoadState) | (t == P - 1 ? ra::kWriteOut : ra::kStoreState);
+      p.scale_log2 = to_log2_scale(sc);
+      const long pi = prof_begin(stream);
+      RA_HIP(launch_fold(p, dt, (int)d, stream), "fold launch");
+      prof_end(pi, stream);
+    }
+    // The slot read by this step is refilled two steps later.
+    if (t >= 1 && t + 2 <= P - 1 && !serial) RA_HIP(hipEventRecord(dr->freed[slot_of(t)], stream), "hipEventRecord");
+  }
+  if (!serial) {
+    RA_HIP(hipEventRecord(dr->join, side), "hipEventRecord");
+    RA_HIP(hipStreamWaitEvent(stream, dr->join, 0), "hipStreamWaitEvent");
+  }
+  if (own_ws) RA_HIP(hipFreeAsync(ws, stream), "hipFreeAsync (ring workspace)");
+  return RA_OK;
+}
+
+RA_API ra_status_t ra_profile_folds(int enable) {
+  g_err.clear();
+  std::lock_guard<std::mutex> g(g_prof.mu);
+  g_prof.on = enable != 0;
+  g_prof.used = 0;
+  return RA_OK;
+}
+
+RA_API ra_status_t ra_profile_read(int64_t* launches, double* total_ms, double* max_ms) {
+  g_err.clear();
+  if (!launches || !total_ms || !max_ms) return fail(RA_E_INVALID_ARG, "output pointer is NULL");
+  std::lock_guard<std::mutex> g(g_prof.mu);
+  double tot = 0.0, mx = 0.0;
+  for (size_t i = 0; i < g_prof.used; ++i) {
+    RA_HIP(hipEventSynchronize(g_prof.ev[2 * i + 1]), "hipEventSynchronize");
+    float ms = 0.0f;
+    RA_HIP(hipEventElapsedTime(&ms, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]), "hipEventElapsedTime");
+    tot += ms;
+    if (ms > mx) mx = ms;
+  }
+  *launches = (int64_t)g_prof.used;
+  *total_ms = tot;
+  *max_ms = mx;
+  g_prof.used = 0;
+  return RA_OK;
+}

@@ -1,0 +1,83 @@
+// State set-up and finalisation kernels.
+//  * init: (m, l, o) = (-inf, 0, 0)  -- aicassindra.com "Ring Attention, math",
+//    "Accumulation math, step by step", the state before the first block.
+//  * finalize: O = o / l -- same passage, after the last block.  A row that
+//    never saw a key (l == 0) is written as 0.
+// Both are plain HBM-bound elementwise passes with 16-byte accesses.
+#include <math.h>
+
+#include "kernels.h"
+
+namespace ra {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void state_init_kernel(float* m, float* l, float* o, int64_t rows, int64_t o_vec4) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < o_vec4; i += stride)
+    ((f32x4*)o)[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < rows; i += stride) {
+    m[i] = -INFINITY;
+    l[i] = 0.0f;
+  }
+}
+
+template <bool kBf16>
+__global__ __launch_bounds__(256) void finalize_kernel(const float* l, const float* o, void* out, int64_t out_sb,
+                                                       int64_t out_sh, int64_t out_sr, int H, int64_t rows, int d,
+                                                       int64_t n_vec4) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int per_row = d / 4;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_vec4; i += stride) {
+    const int64_t row_all = i / per_row;  // (bi * H + hi) * rows + row
+    const int c = (int)(i % per_row) * 4;
+    const int64_t bh = row_all / rows;
+    const int64_t row = row_all % rows;
+    const int64_t bi = bh / H;
+    const int64_t hi = bh % H;
+    const float lv = l[row_all];
+    const float inv = lv > 0.0f ? 1.0f / lv : 0.0f;
+    const f32x4 t = ((const f32x4*)o)[i];
+    const int64_t off = bi * out_sb + hi * out_sh + row * out_sr + c;
+    if (kBf16) {
+      bf16x4 r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[e] = (__bf16)(t[e] * inv);
+      *(bf16x4*)((__bf16*)out + off) = r;
+    } else {
+      f32x4 r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[e] = t[e] * inv;
+      *(f32x4*)((float*)out + off) = r;
+    }
+  }
+}
+
+inline unsigned grid_for(int64_t n) {
+  const int64_t g = (n + 255) / 256;
+  return (unsigned)(g < 1 ? 1 : (g > 65536 ? 65536 : g));
+}
+
+}  // namespace
+
+hipError_t launch_state_init(float* m, float* l, float* o, int64_t rows_total, int d, hipStream_t s) {
+  const int64_t o_vec4 = rows_total * d / 4;
+  if (rows_total <= 0) return hipSuccess;
+  state_init_kernel<<<grid_for(o_vec4), 256, 0, s>>>(m, l, o, rows_total, o_vec4);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize(const float* l, const float* o, void* out, bool out_bf16, int64_t out_sb,
+                           int64_t out_sh, int64_t out_sr, int B, int H, int64_t rows, int d, hipStream_t s) {
+  const int64_t n_vec4 = (int64_t)B * H * rows * d / 4;
+  if (n_vec4 <= 0) return hipSuccess;
+  if (out_bf16)
+    finalize_kernel<true><<<grid_for(n_vec4), 256, 0, s>>>(l, o, out, out_sb, out_sh, out_sr, H, rows, d, n_vec4);
+  else
+    finalize_kernel<false><<<grid_for(n_vec4), 256, 0, s>>>(l, o, out, out_sb, out_sh, out_sr, H, rows, d, n_vec4);
+  return hipGetLastError();
+}
+
+}  // namespace ra

@@ -1,0 +1,159 @@
+/*
+ * ra.h -- C ABI of the ring-attention fold library (libra.so) for AMD MI355X (gfx950).
+ *
+ * The operation is one device's share of Ring Attention:
+ *
+ *   * the fold (aicassindra.com "Ring Attention, math", the per-query
+ *     pseudo-code under "The online-softmax identity that makes streaming
+ *     legal"; bembew.net "Ring Attention", "Conceptual Algorithm"):
+ *     for every query row, with the visiting block's scores s = q.k / sqrt(d),
+ *        m' = max(m, max_j s_j),  alpha = exp(m - m'),
+ *        l' = alpha*l + sum_j exp(s_j - m'),
+ *        o' = alpha*o + sum_j exp(s_j - m') * v_j;
+ *   * the ring loop (same page, "The ring schedule" and "Accumulation math,
+ *     step by step"): device i folds block (i - t) mod P on step t = 0..P-1,
+ *     starting from (m, l, o) = (-inf, 0, 0) with its own block, then O_i = o / l.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *   * Tensors q, k, v, out have logical shape [B, H, rows, d] with the d axis
+ *     contiguous; their strides are given in ELEMENTS as {batch, head, row}.
+ *     Every such pointer must be 16-byte aligned and every stride a multiple of
+ *     8 elements (bf16) or 4 elements (fp32).
+ *   * The running state is float32 and contiguous: m, l are [B, H, rows]; o is
+ *     [B, H, rows, d].  m is in natural-log units of the scaled scores, exactly
+ *     as the pages define it, so it can be compared with any reference.
+ *   * All data pointers are DEVICE pointers owned by the caller.  The library
+ *     never frees caller memory; it owns only its optional internal workspace
+ *     and a cached side stream plus events per device.
+ *   * `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Every call only enqueues work and returns; all of it, including work on
+ *     the library's side stream, is ordered before later work on `stream`.
+ *   * scale: 0 selects 1/sqrt(d); otherwise it must be finite and > 0.
+ *   * d must be 64, 128 or 256.
+ *   * Arguments are checked on the host before any GPU work; a bad argument
+ *     returns RA_E_INVALID_ARG / RA_E_UNSUPPORTED, launches nothing and sets
+ *     the text returned by ra_last_error().  HIP failures return RA_E_HIP or
+ *     RA_E_OOM.  No C++ exception crosses this boundary.
+ *   * No atomics are used: results are bitwise reproducible run to run on the
+ *     same GPU and build.
+ */
+#ifndef RA_H
+#define RA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RA_OK = 0,
+  RA_E_INVALID_ARG = 1, /* null pointer, bad size, bad stride, bad scale, workspace too small */
+  RA_E_UNSUPPORTED = 2, /* valid request this build does not implement (d, N % P != 0, ...) */
+  RA_E_HIP = 3,         /* a HIP runtime call or kernel launch failed */
+  RA_E_OOM = 4          /* the internal workspace could not be allocated */
+} ra_status_t;
+
+typedef enum { RA_DTYPE_F32 = 0, RA_DTYPE_BF16 = 1 } ra_dtype_t;
+
+/*
+ * ra_state_init -- set (m, l, o) = (-inf, 0, 0) for B*H*rows query rows.
+ * Math page, "Accumulation math, step by step" (loop set-up).
+ * m, l: [B, H, rows] float32; o: [B, H, rows, d] float32; all contiguous.
+ * rows == 0 is a no-op.
+ */
+ra_status_t ra_state_init(float* m, float* l, float* o, int64_t B, int64_t H, int64_t rows, int64_t d,
+                          void* stream);
+
+/*
+ * ra_fold_block -- fold ONE visiting K/V block into the running state.
+ * Math page, the per-query pseudo-code under the online-softmax identity;
+ * bembew.net "Conceptual Algorithm", the loop body.
+ *
+ * q: [B, H, q_rows, d], k and v: [B, H, kv_rows, d], all of dtype `dt`, strides
+ * in elements {batch, head, row}.  m, l, o: the state of the q_rows query rows
+ * (layout above), read and updated in place.  Scores are computed with fp32
+ * accumulation; for bf16 the weights exp(s - m') are rounded to bf16 before
+ * the value product and l sums the same rounded weights.  Blocks may be folded
+ * in any order (the math page's worked example: the result does not depend on
+ * the order).  kv_rows == 0 leaves the state unchanged; q_rows == 0 is a no-op.
+ * Any q_rows, kv_rows >= 0 are accepted (ragged tails are masked).
+ */
+ra_status_t ra_fold_block(const void* q, const int64_t q_strides[3], const void* k, const int64_t k_strides[3],
+                          const void* v, const int64_t v_strides[3], ra_dtype_t dt, int64_t B, int64_t H,
+                          int64_t q_rows, int64_t kv_rows, int64_t d, float scale, float* m, float* l, float* o,
+                          void* stream);
+
+/*
+ * ra_finalize -- O = o / l after the last block (math page, end of the loop).
+ * l: [B, H, rows], o: [B, H, rows, d] (float32, contiguous); out: [B, H, rows, d]
+ * of dtype out_dt with strides out_strides (elements).  Rows with l == 0 (never
+ * folded) are written as 0.  The cast to bf16 rounds to nearest even.
+ */
+ra_status_t ra_finalize(const float* l, const float* o, void* out, const int64_t out_strides[3], ra_dtype_t out_dt,
+                        int64_t B, int64_t H, int64_t rows, int64_t d, void* stream);
+
+/*
+ * ra_ring_workspace_bytes -- device workspace ra_ring_forward needs: the fp32
+ * state of the n_q resident query blocks plus, per resident block, the
+ * visiting K/V double buffer (two blocks, not P: math page, "Memory: O(1)
+ * extra per device").  Returns 0 for arguments ra_ring_forward would reject.
+ */
+size_t ra_ring_workspace_bytes(ra_dtype_t dt, int64_t B, int64_t H, int64_t N, int64_t d, int32_t P,
+                               int32_t n_q);
+
+/*
+ * ra_ring_forward -- the whole per-device loop for n_q resident query blocks
+ * of a P-device ring, run as P virtual ring steps on one GPU.
+ * Math page, "Sharding the sequence", "The ring schedule", "Accumulation math,
+ * step by step"; bembew.net "Conceptual Algorithm".
+ *
+ * q:   [B, H, n_q*b, d] -- the resident query blocks stacked along rows in
+ *      query_blocks order (b = N/P); strides q_strides.
+ * k,v: [B, H, N, d] -- the whole sequence; block j is rows [j*b, (j+1)*b).
+ * out: [B, H, n_q*b, d] -- like q; receives O_i = o / l.
+ * query_blocks: HOST array of n_q block ids in [0, P); NULL means 0..P-1
+ *      (then n_q must equal P).
+ * On step t resident block i folds block (i - t) mod P.  Step 0 reads the own
+ * block in place; the next block is copied into the other half of a per-block
+ * double buffer by hipMemcpy2DAsync on a side stream while the current step's
+ * fold runs (the stand-in for the ring's send to i+1 / receive from i-1),
+ * ordered by events.
+ * workspace: device buffer of at least ra_ring_workspace_bytes(...) bytes,
+ *      256-byte aligned, or NULL to let the library allocate and free one in
+ *      stream order.  Two calls that share a workspace must be ordered on
+ *      their streams.
+ * N % P != 0 returns RA_E_UNSUPPORTED.
+ */
+ra_status_t ra_ring_forward(const void* q, const int64_t q_strides[3], const void* k, const int64_t k_strides[3],
+                            const void* v, const int64_t v_strides[3], void* out, const int64_t out_strides[3],
+                            ra_dtype_t dt, int64_t B, int64_t H, int64_t N, int64_t d, int32_t P,
+                            const int32_t* query_blocks, int32_t n_q, float scale, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
+ * Measurement support (not part of the method).  While enabled on the calling
+ * process, ra_ring_forward records a HIP event pair around every fold launch,
+ * on the caller's stream that the launch uses.  ra_profile_read waits for the
+ * recorded events, returns the number of fold launches, their summed and
+ * largest durations in milliseconds, and clears the record.  Enabling or
+ * disabling also clears it.  At most 4096 launches are recorded; later ones
+ * are not timed (the count says how many were).
+ */
+ra_status_t ra_profile_folds(int enable);
+ra_status_t ra_profile_read(int64_t* launches, double* total_ms, double* max_ms);
+
+/* Text of the last error on the calling thread ("" after success).  Valid
+ * until the next ra_* call on the same thread. */
+const char* ra_last_error(void);
+
+/* Library version, "major.minor.patch". */
+const char* ra_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RA_H */

@@ -1,0 +1,137 @@
+"""The C ABI without a GPU: the library loads, exports every symbol
+include/ra.h declares, and rejects bad arguments on the host before any HIP
+call (so these run in a GPU-less container)."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ra.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import blockwise_online_softmax_fold_amd as ra
+
+    if not os.path.exists(ra.lib_path()):
+        from blockwise_online_softmax_fold_amd import build
+
+        build.build()
+    return ra.load()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ra_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    import blockwise_online_softmax_fold_amd as ra
+
+    assert _declared() == sorted(ra.EXPORTED)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+    # and nothing of the kernels' internals leaks
+    import subprocess
+
+    out = subprocess.run(["nm", "-D", "--defined-only", lib._name], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert {n for n in exported if n.startswith("ra_")} == set(_declared())
+
+
+def test_version(lib):
+    assert re.match(r"^\d+\.\d+\.\d+$", lib.ra_version().decode())
+
+
+# fake, well-aligned device addresses: every call below must fail validation
+# before it could use them
+A = ctypes.c_void_p(0x10000)
+S_BF16 = (ctypes.c_int64 * 3)(16 * 1024 * 128, 1024 * 128, 128)
+BF16, F32 = 1, 0
+
+
+def _fold(lib, q=A, qs=S_BF16, k=A, ks=S_BF16, v=A, vs=S_BF16, dt=BF16, B=1, H=16, q_rows=1024, kv_rows=1024,
+          d=128, scale=0.0, m=A, l=A, o=A):
+    return lib.ra_fold_block(q, qs, k, ks, v, vs, dt, B, H, q_rows, kv_rows, d, ctypes.c_float(scale), m, l, o, None)
+
+
+@pytest.mark.parametrize("kwargs,status,needle", [
+    (dict(q=ctypes.c_void_p(None)), 1, "q is NULL"),
+    (dict(k=ctypes.c_void_p(0x10008)), 1, "16-byte aligned"),
+    (dict(d=96), 2, "head dim"),
+    (dict(dt=7), 1, "dtype"),
+    (dict(B=0), 1, "must be >= 1"),
+    (dict(q_rows=-1), 1, ">= 0"),
+    (dict(scale=-1.0), 1, "scale"),
+    (dict(scale=float("nan")), 1, "scale"),
+    (dict(vs=(ctypes.c_int64 * 3)(16, 8, 4)), 1, "multiple of 8"),
+    (dict(m=ctypes.c_void_p(None)), 1, "NULL"),
+    (dict(o=ctypes.c_void_p(0x10004)), 1, "o is not 16-byte aligned"),
+])
+def test_fold_block_rejects(lib, kwargs, status, needle):
+    assert _fold(lib, **kwargs) == status
+    assert needle in lib.ra_last_error().decode()
+
+
+def test_fold_block_empty_is_ok_without_gpu(lib):
+    assert _fold(lib, q_rows=0) == 0
+    assert _fold(lib, kv_rows=0) == 0
+    assert lib.ra_last_error().decode() == ""
+
+
+def _ring(lib, dt=BF16, B=1, H=32, N=131072, d=128, P=16, qb=None, n_q=16, scale=0.0, ws=None, ws_bytes=0,
+          q=A, out=A):
+    qbp = None if qb is None else (ctypes.c_int32 * len(qb))(*qb)
+    return lib.ra_ring_forward(q, S_BF16, A, S_BF16, A, S_BF16, out, S_BF16, dt, B, H, N, d, P, qbp, n_q,
+                               ctypes.c_float(scale), ws if ws is not None else ctypes.c_void_p(None), ws_bytes,
+                               None)
+
+
+@pytest.mark.parametrize("kwargs,status,needle", [
+    (dict(N=1000, P=16), 2, "not a multiple"),
+    (dict(P=0), 1, "P=0"),
+    (dict(N=8, P=16), 1, ">= P"),
+    (dict(n_q=4), 1, "n_q=4 != P=16"),
+    (dict(qb=[0, 16], n_q=2), 1, "outside"),
+    (dict(qb=[-1], n_q=1), 1, "outside"),
+    (dict(d=32), 2, "head dim"),
+    (dict(out=ctypes.c_void_p(None)), 1, "out is NULL"),
+    (dict(ws=ctypes.c_void_p(0x10000), ws_bytes=1024), 1, "smaller than"),
+    (dict(scale=float("inf")), 1, "scale"),
+])
+def test_ring_forward_rejects(lib, kwargs, status, needle):
+    assert _ring(lib, **kwargs) == status
+    assert needle in lib.ra_last_error().decode()
+
+
+def test_ring_workspace_is_two_blocks_not_P(lib):
+    """Math page, "Memory": besides its own shard a device holds at most two
+    visiting K/V blocks, whatever P is."""
+    B, H, d, n_q = 1, 8, 128, 1
+    sizes = {}
+    for P in (1, 2, 4, 16, 64):
+        b = 4096
+        N = b * P
+        sizes[P] = lib.ra_ring_workspace_bytes(BF16, B, H, N, d, P, n_q)
+        state = B * H * b * (d + 2) * 4
+        blocks = min(2, P - 1) * 2 * B * H * b * d * 2  # K and V, bf16
+        assert state + blocks <= sizes[P] <= state + blocks + 5 * 256
+    assert sizes[4] == sizes[16] == sizes[64]
+    assert lib.ra_ring_workspace_bytes(BF16, 1, 1, 1000, 128, 16, 1) == 0  # rejected shape
+
+
+def test_state_init_and_finalize_reject(lib):
+    assert lib.ra_state_init(A, A, ctypes.c_void_p(0x10004), 1, 1, 4, 64, None) == 1
+    assert lib.ra_state_init(A, A, A, 1, 1, 4, 48, None) == 2
+    assert lib.ra_state_init(A, A, A, 1, 1, 0, 64, None) == 0
+    assert lib.ra_finalize(A, A, ctypes.c_void_p(None), S_BF16, BF16, 1, 1, 4, 64, None) == 1
+    assert lib.ra_finalize(A, A, A, S_BF16, 9, 1, 1, 4, 64, None) == 1
