@@ -269,8 +269,8 @@ RA_API ra_status_t ra_state_init(float* m, float* l, float* o, int64_t B, int64_
   ra_status_t st = check_common(RA_DTYPE_F32, B, H, d);
   if (st != RA_OK) return st;
   if (rows < 0) return fail(RA_E_INVALID_ARG, "rows=%lld must be >= 0", (long long)rows);
-  if ((st = check_state(m, l, o)) != RA_OK) return st;
   if (rows == 0) return RA_OK;
+  if ((st = check_state(m, l, o)) != RA_OK) return st;
   RA_HIP(ra::launch_state_init(m, l, o, B * H * rows, (int)d, (hipStream_t)stream), "state init launch");
   return RA_OK;
 }
@@ -287,11 +287,12 @@ RA_API ra_status_t ra_fold_block(const void* q, const int64_t q_strides[3], cons
     return fail(RA_E_UNSUPPORTED, "q_rows or kv_rows is too large for one launch");
   float sc;
   if ((st = resolve_scale(scale, d, &sc)) != RA_OK) return st;
+  if (q_rows == 0) return RA_OK;  // no query rows: nothing is read or written
   if ((st = check_tensor("q", q, q_strides, dt)) != RA_OK) return st;
+  if ((st = check_state(m, l, o)) != RA_OK) return st;
+  if (kv_rows == 0) return RA_OK;  // an empty block leaves the state as it is
   if ((st = check_tensor("k", k, k_strides, dt)) != RA_OK) return st;
   if ((st = check_tensor("v", v, v_strides, dt)) != RA_OK) return st;
-  if ((st = check_state(m, l, o)) != RA_OK) return st;
-  if (q_rows == 0 || kv_rows == 0) return RA_OK;  // nothing to fold
 
   FoldParams p = {};
   p.q = q;
@@ -324,10 +325,10 @@ RA_API ra_status_t ra_finalize(const float* l, const float* o, void* out, const 
   ra_status_t st = check_common(out_dt, B, H, d);
   if (st != RA_OK) return st;
   if (rows < 0) return fail(RA_E_INVALID_ARG, "rows=%lld must be >= 0", (long long)rows);
+  if (rows == 0) return RA_OK;
   if (l == nullptr || o == nullptr) return fail(RA_E_INVALID_ARG, "state pointer l or o is NULL");
   if (((uintptr_t)o & 15) != 0) return fail(RA_E_INVALID_ARG, "state o is not 16-byte aligned");
   if ((st = check_tensor("out", out, out_strides, out_dt)) != RA_OK) return st;
-  if (rows == 0) return RA_OK;
   RA_HIP(ra::launch_finalize(l, o, out, out_dt == RA_DTYPE_BF16, out_strides[0], out_strides[1], out_strides[2],
                              (int)B, (int)H, rows, (int)d, (hipStream_t)stream),
          "finalize launch");

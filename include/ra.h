@@ -62,7 +62,7 @@ typedef enum { RA_DTYPE_F32 = 0, RA_DTYPE_BF16 = 1 } ra_dtype_t;
  * ra_state_init -- set (m, l, o) = (-inf, 0, 0) for B*H*rows query rows.
  * Math page, "Accumulation math, step by step" (loop set-up).
  * m, l: [B, H, rows] float32; o: [B, H, rows, d] float32; all contiguous.
- * rows == 0 is a no-op.
+ * rows == 0 is a no-op (the pointers may then be NULL).
  */
 ra_status_t ra_state_init(float* m, float* l, float* o, int64_t B, int64_t H, int64_t rows, int64_t d,
                           void* stream);
@@ -78,8 +78,9 @@ ra_status_t ra_state_init(float* m, float* l, float* o, int64_t B, int64_t H, in
  * accumulation; for bf16 the weights exp(s - m') are rounded to bf16 before
  * the value product and l sums the same rounded weights.  Blocks may be folded
  * in any order (the math page's worked example: the result does not depend on
- * the order).  kv_rows == 0 leaves the state unchanged; q_rows == 0 is a no-op.
- * Any q_rows, kv_rows >= 0 are accepted (ragged tails are masked).
+ * the order).  kv_rows == 0 leaves the state unchanged (k and v may then be
+ * NULL); q_rows == 0 is a no-op (every pointer may then be NULL).  Any
+ * q_rows, kv_rows >= 0 are accepted (ragged tails are masked).
  */
 ra_status_t ra_fold_block(const void* q, const int64_t q_strides[3], const void* k, const int64_t k_strides[3],
                           const void* v, const int64_t v_strides[3], ra_dtype_t dt, int64_t B, int64_t H,
@@ -91,6 +92,7 @@ ra_status_t ra_fold_block(const void* q, const int64_t q_strides[3], const void*
  * l: [B, H, rows], o: [B, H, rows, d] (float32, contiguous); out: [B, H, rows, d]
  * of dtype out_dt with strides out_strides (elements).  Rows with l == 0 (never
  * folded) are written as 0.  The cast to bf16 rounds to nearest even.
+ * rows == 0 is a no-op (the pointers may then be NULL).
  */
 ra_status_t ra_finalize(const float* l, const float* o, void* out, const int64_t out_strides[3], ra_dtype_t out_dt,
                         int64_t B, int64_t H, int64_t rows, int64_t d, void* stream);

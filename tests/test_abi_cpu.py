@@ -83,9 +83,13 @@ def test_fold_block_rejects(lib, kwargs, status, needle):
 
 
 def test_fold_block_empty_is_ok_without_gpu(lib):
+    N = ctypes.c_void_p(None)
     assert _fold(lib, q_rows=0) == 0
+    assert _fold(lib, q_rows=0, q=N, k=N, v=N, m=N, l=N, o=N) == 0
     assert _fold(lib, kv_rows=0) == 0
+    assert _fold(lib, kv_rows=0, k=N, v=N) == 0
     assert lib.ra_last_error().decode() == ""
+    assert _fold(lib, kv_rows=0, q=N) == 1  # query rows still need q
 
 
 def _ring(lib, dt=BF16, B=1, H=32, N=131072, d=128, P=16, qb=None, n_q=16, scale=0.0, ws=None, ws_bytes=0,

@@ -123,6 +123,14 @@ def test_fold_block_zero_rows_is_noop(ra):
     ra.ra_finalize(l, o, out)
     torch.cuda.synchronize()
     assert torch.all(out == 0)
+    # no query rows at all
+    q0 = torch.empty((1, 1, 0, 128), device="cuda", dtype=torch.bfloat16)
+    m0, l0, o0 = _new_state(1, 1, 0, 128)
+    kk = torch.randn((1, 1, 64, 128), device="cuda").bfloat16()
+    ra.ra_state_init(m0, l0, o0)
+    ra.ra_fold_block(q0, kk, kk, m0, l0, o0)
+    ra.ra_finalize(l0, o0, q0)
+    torch.cuda.synchronize()
 
 
 # ---------------------------------------------------------------------------
