@@ -106,6 +106,8 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run one plain 1 GiB device copy (a known-size reference for HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -134,6 +136,14 @@ def main() -> int:
 
     def step():
         ra.ra_ring_forward(q, k, v, w.P, query_blocks=qb, out=out, workspace=ws)
+
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print("[bench] calibration copy: 1 GiB read + 1 GiB written", file=sys.stderr, flush=True)
+        del src, dst
 
     for _ in range(args.warmup):
         step()

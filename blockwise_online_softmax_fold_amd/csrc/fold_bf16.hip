@@ -48,7 +48,6 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;
 constexpr int kTileQ = kWaves * 32;  // query rows per workgroup
-constexpr int kTileK = 64;           // keys per LDS tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -86,16 +85,46 @@ __device__ inline s16x4 lds_tr16(const __bf16* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
 }
 
+// Keys per LDS tile for each head dim.
 template <int D>
-__global__ __launch_bounds__(256) void fold_bf16_kernel(const FoldParams p) {
-  constexpr int KS = D + 8;   // LDS row pitch of K (elements): 16 B mod 128 B per row
-  constexpr int VS = D + 16;  // LDS row pitch of V: 32 B mod 128 B per row
-  constexpr int NC = D / 16;  // 16-wide d chunks of the score contraction
-  constexpr int NDB = D / 32; // 32-wide d blocks of the output
-  constexpr int CPR = D / 8;  // 16-byte chunks per K/V row
-  constexpr int CH = kTileK * CPR / 256;  // 16-byte chunks per thread per tile
-  __shared__ __attribute__((aligned(16))) __bf16 ks[kTileK * KS];
-  __shared__ __attribute__((aligned(16))) __bf16 vs[kTileK * VS];
+struct TileCfg {
+  static constexpr int TK = D >= 256 ? 32 : 64;
+};
+
+// XOR swizzle of the 16-byte units of LDS row r.  K is read as 16-byte
+// units of 16 consecutive rows and V as 8-byte transposed reads of 4 rows x 4
+// units; with the 64-bank LDS both patterns are conflict-free when f is a
+// bijection on 16 consecutive rows whose bits 2..3 differ across 4 consecutive
+// rows (rows of 128 B for d = 64 pair up within one 256-byte bank row, hence
+// the separate form).
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D >= 128)
+    return ((r & 3) << 2) | ((r >> 2) & 3);
+  else
+    return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+// 16 bytes from global memory straight into LDS (global_load_lds_dwordx4):
+// lane i's bytes land at lds_wave_base + 16 i.
+__device__ __forceinline__ void gload_lds16(const __bf16* g, __bf16* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(g),
+                                   (__attribute__((address_space(3))) void*)(lds_wave_base), 16, 0, 0);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1 : 2)))
+void fold_bf16_kernel(const FoldParams p) {
+  constexpr int TK = TileCfg<D>::TK;
+  constexpr int NKB = TK / 32;          // 32-key blocks per tile
+  constexpr int NC = D / 16;            // 16-wide d chunks of the score contraction
+  constexpr int NDB = D / 32;           // 32-wide d blocks of the output
+  constexpr int UPR = D / 8;            // 16-byte units per K/V row
+  constexpr int TE = TK * D;            // elements of one K (or V) tile
+  constexpr int CPW = TE / 512 / 4;     // 1 KB direct-load chunks per wave per tensor
+  static_assert(CPW >= 1 && TE % 2048 == 0, "tile must split into whole 1 KB chunks per wave");
+  // Two buffers, each a K tile followed by a V tile, rows unpadded, units swizzled.
+  __shared__ __attribute__((aligned(1024))) __bf16 lds[2 * 2 * TE];
 
   const int tiles_q = (p.q_rows + kTileQ - 1) / kTileQ;
   const int total = tiles_q * p.n_res * p.H * p.B;
@@ -108,7 +137,7 @@ __global__ __launch_bounds__(256) void fold_bf16_kernel(const FoldParams p) {
   const int bi = w / p.H;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int lr = lane & 31;
   const int lg = lane >> 5;
@@ -155,54 +184,95 @@ __global__ __launch_bounds__(256) void fold_bf16_kernel(const FoldParams p) {
 
   const __bf16* kbase = (const __bf16*)p.k + bi * p.k_sb + hi * p.k_sh + p.k_off[r];
   const __bf16* vbase = (const __bf16*)p.v + bi * p.v_sb + hi * p.v_sh + p.v_off[r];
-  const int n_kt = (p.kv_rows + kTileK - 1) / kTileK;
+  const int n_kt = (p.kv_rows + TK - 1) / TK;
   const float c2 = p.scale_log2;
 
-  // LDS addresses of this lane's operand reads.
-  const __bf16* ka = ks + lr * KS + 8 * lg;  // + (32 kb) * KS + 16 c
-  const int tr_row = 4 * lg + ((lane & 15) >> 2);
-  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const __bf16* va = vs + tr_row * VS + tr_col;  // + (32 kb + 16 c [+ 8]) * VS + 32 db
+  // Direct-load addressing: chunk c of a tile is LDS units [64c, 64c + 64);
+  // lane i writes unit 64c + i = (row, pos) and so fetches global unit
+  // pos ^ swz(row) of that row.
+  // (The host guarantees row strides below 2^24 elements, so these fit in 32 bits.)
+  const int k_sr = (int)p.k_sr, v_sr = (int)p.v_sr;
+  int ld_koff[CPW], ld_voff[CPW];
+#pragma unroll
+  for (int j = 0; j < CPW; ++j) {
+    const int u = (wave * CPW + j) * 64 + lane;
+    const int lrow = u / UPR;
+    const int gunit = (u % UPR) ^ swz<D>(lrow);
+    ld_koff[j] = lrow * k_sr + gunit * 8;
+    ld_voff[j] = lrow * v_sr + gunit * 8;
+  }
+  auto issue_tile = [&](int kt, int buf) {
+    const int key0 = kt * TK;
+    __bf16* kl = lds + buf * 2 * TE + wave * CPW * 512;
+    __bf16* vl = kl + TE;
+    if (key0 + TK <= p.kv_rows) {
+      const __bf16* kg = kbase + (int64_t)key0 * k_sr;
+      const __bf16* vg = vbase + (int64_t)key0 * v_sr;
+#pragma unroll
+      for (int j = 0; j < CPW; ++j) {
+        gload_lds16(kg + ld_koff[j], kl + j * 512);
+        gload_lds16(vg + ld_voff[j], vl + j * 512);
+      }
+    } else {  // ragged last tile: rows past the end re-read the last row
+#pragma unroll
+      for (int j = 0; j < CPW; ++j) {
+        const int u = (wave * CPW + j) * 64 + lane;
+        const int lrow = u / UPR;
+        const int gunit = (u % UPR) ^ swz<D>(lrow);
+        const int64_t g = min(key0 + lrow, p.kv_rows - 1);
+        gload_lds16(kbase + g * k_sr + gunit * 8, kl + j * 512);
+        gload_lds16(vbase + g * v_sr + gunit * 8, vl + j * 512);
+      }
+    }
+  };
 
+  // LDS read addressing (element offsets inside a K or V tile).
+  // K (A operand of S^T): row 32kb + lr, unit 2c + lg  -> ((2c) ^ gk) with gk = lg ^ swz(lr).
+  const int gk = lg ^ swz<D>(lr);
+  int k_rd[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) k_rd[c] = lr * D + (((2 * c) ^ gk) << 3);
+  // V (A operand of O^T, transposed reads): row 32kb + 16c + vr (+8), column
+  // 32db + 16h + 4(lane & 3), i.e. unit (4db + x) with x = 2h + ((lane & 3) >> 1).
+  const int vr = 4 * lg + ((lane & 15) >> 2);
+  const int vx = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  int v_rd[2][NDB];
+#pragma unroll
+  for (int run = 0; run < 2; ++run) {
+    const int rr = vr + 8 * run;
+    const int y = vx ^ swz<D>(rr);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) v_rd[run][db] = rr * D + (((4 * db) ^ y) << 3) + 4 * (lane & 1);
+  }
+
+  if (n_kt > 0) issue_tile(0, 0);
   for (int kt = 0; kt < n_kt; ++kt) {
-    const int key0 = kt * kTileK;
-    bf16x8 kreg[CH], vreg[CH];
-#pragma unroll
-    for (int u = 0; u < CH; ++u) {
-      const int ch = tid + 256 * u;
-      const int rr = ch / CPR;
-      const int cc = (ch % CPR) * 8;
-      const int64_t g = min(key0 + rr, p.kv_rows - 1);
-      kreg[u] = *(const bf16x8*)(kbase + g * p.k_sr + cc);
-      vreg[u] = *(const bf16x8*)(vbase + g * p.v_sr + cc);
-    }
-    __syncthreads();  // previous tile fully consumed
-#pragma unroll
-    for (int u = 0; u < CH; ++u) {
-      const int ch = tid + 256 * u;
-      const int rr = ch / CPR;
-      const int cc = (ch % CPR) * 8;
-      *(bf16x8*)(ks + rr * KS + cc) = kreg[u];
-      *(bf16x8*)(vs + rr * VS + cc) = vreg[u];
-    }
+    const int buf = kt & 1;
+    const int key0 = kt * TK;
+    // Tile kt landed (this wave's loads), then every wave's loads and every
+    // wave's reads of the other buffer (previous iteration) are complete.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
+    if (kt + 1 < n_kt) issue_tile(kt + 1, buf ^ 1);
+    const __bf16* kl = lds + buf * 2 * TE;
+    const __bf16* vl = kl + TE;
 
-    // S^T for two 32-key blocks: sacc[kb][i] is the score of query row `row`
+    // S^T for the 32-key blocks: sacc[kb][i] is the score of query row `row`
     // against key key0 + 32 kb + 8 (i / 4) + 4 lg + i % 4.
-    f32x16 sacc[2];
+    f32x16 sacc[NKB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.0f;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const bf16x8 a = *(const bf16x8*)(ka + 32 * kb * KS + 16 * c);
+        const bf16x8 a = *(const bf16x8*)(kl + 32 * kb * D + k_rd[c]);
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], sacc[kb], 0, 0, 0);
       }
     }
-    if (key0 + kTileK > p.kv_rows) {  // ragged last tile: keys past the end get -inf
+    if (key0 + TK > p.kv_rows) {  // ragged last tile: keys past the end get -inf
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = key0 + 32 * kb + 8 * (i >> 2) + 4 * lg + (i & 3);
@@ -212,7 +282,7 @@ __global__ __launch_bounds__(256) void fold_bf16_kernel(const FoldParams p) {
 
     float mx = sacc[0][0];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
     mx = pair_max(mx);
@@ -222,10 +292,10 @@ __global__ __launch_bounds__(256) void fold_bf16_kernel(const FoldParams p) {
     const float alpha = __builtin_amdgcn_exp2f(mc - m_new);
     mc = m_new;
 
-    unsigned pk[2][8];
+    unsigned pk[NKB][8];
     float lsum = 0.0f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][2 * j], c2, -m_new));
@@ -234,25 +304,29 @@ __global__ __launch_bounds__(256) void fold_bf16_kernel(const FoldParams p) {
         lsum = sum_bf16_pair(pk[kb][j], lsum);
       }
     lpart = fmaf(lpart, alpha, lsum);
+    // o is rescaled only when some row of this wave raised its maximum
+    // (alpha == 1 exactly otherwise).
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+    }
 
     // O^T += V^T P^T.  For key chunk (kb, c) the lane's B operand is its
     // weights i = 8c .. 8c+7 of block kb, i.e. keys 32kb+16c+4lg+{0..3} and
     // 32kb+16c+8+4lg+{0..3}; the A operand holds V at the same keys, column d.
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const u32x4 bw = {pk[kb][4 * c], pk[kb][4 * c + 1], pk[kb][4 * c + 2], pk[kb][4 * c + 3]};
         const bf16x8 b = __builtin_bit_cast(bf16x8, bw);
-        const __bf16* vrow = va + (32 * kb + 16 * c) * VS;
+        const __bf16* vrow = vl + (32 * kb + 16 * c) * D;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const s16x4 t0 = lds_tr16(vrow + 32 * db);
-          const s16x4 t1 = lds_tr16(vrow + 8 * VS + 32 * db);
+          const s16x4 t0 = lds_tr16(vrow + v_rd[0][db]);
+          const s16x4 t1 = lds_tr16(vrow + v_rd[1][db]);
           const u32x2 w0 = __builtin_bit_cast(u32x2, t0);
           const u32x2 w1 = __builtin_bit_cast(u32x2, t1);
           const u32x4 aw = {w0[0], w0[1], w1[0], w1[1]};

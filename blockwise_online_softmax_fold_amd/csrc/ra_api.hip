@@ -64,6 +64,14 @@ ra_status_t check_tensor(const char* name, const void* ptr, const int64_t* strid
   return RA_OK;
 }
 
+// The fold kernels address one K/V tile with 32-bit row offsets.
+constexpr int64_t kMaxKvRowStride = (int64_t)1 << 24;
+ra_status_t check_kv_row_stride(const char* name, const int64_t* strides) {
+  if (strides[2] >= kMaxKvRowStride)
+    return fail(RA_E_UNSUPPORTED, "%s row stride %lld is not below 2^24 elements", name, (long long)strides[2]);
+  return RA_OK;
+}
+
 ra_status_t check_state(const float* m, const float* l, const float* o) {
   if (!m || !l || !o) return fail(RA_E_INVALID_ARG, "state pointer m, l or o is NULL");
   if (((uintptr_t)o & 15) != 0) return fail(RA_E_INVALID_ARG, "state o is not 16-byte aligned");
@@ -178,6 +186,8 @@ ra_status_t check_ring(const void* q, const int64_t* q_strides, const void* k, c
   if ((st = check_tensor("k", k, k_strides, dt)) != RA_OK) return st;
   if ((st = check_tensor("v", v, v_strides, dt)) != RA_OK) return st;
   if ((st = check_tensor("out", out, out_strides, dt)) != RA_OK) return st;
+  if ((st = check_kv_row_stride("k", k_strides)) != RA_OK) return st;
+  if ((st = check_kv_row_stride("v", v_strides)) != RA_OK) return st;
   return RA_OK;
 }
 
@@ -293,6 +303,8 @@ RA_API ra_status_t ra_fold_block(const void* q, const int64_t q_strides[3], cons
   if (kv_rows == 0) return RA_OK;  // an empty block leaves the state as it is
   if ((st = check_tensor("k", k, k_strides, dt)) != RA_OK) return st;
   if ((st = check_tensor("v", v, v_strides, dt)) != RA_OK) return st;
+  if ((st = check_kv_row_stride("k", k_strides)) != RA_OK) return st;
+  if ((st = check_kv_row_stride("v", v_strides)) != RA_OK) return st;
 
   FoldParams p = {};
   p.q = q;
