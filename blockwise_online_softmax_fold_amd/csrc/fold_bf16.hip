@@ -12,8 +12,10 @@
 //    launch; the state (m, l, o) is loaded once, kept in registers while the
 //    visiting block streams past, and stored once (or normalised and written as
 //    the output on the last ring step).
-//  * The visiting block streams through LDS in 64-key tiles (K and V row-major,
-//    rows padded so both access patterns below are free of bank conflicts).
+//  * The visiting block streams through two LDS buffers in 64-key tiles (32 for
+//    d = 256): K and V row-major, the 16-byte units of each row XOR-swizzled so
+//    both read patterns below are free of bank conflicts, filled straight from
+//    global memory by buffer_load ... lds while the other buffer is in use.
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //    in the accumulator layout a lane then holds 16 scores of ONE query row
 //    (lane % 32) and the other 16 of the 32 keys sit in lane ^ 32, so the row
@@ -27,6 +29,11 @@
 //  * exp is one v_exp_f32 (base 2): log2(e) is folded into the scale.  The row
 //    sum l adds the same bf16-rounded weights that enter the value product
 //    (v_dot2_f32_bf16 against (1, 1)), so numerator and denominator agree.
+//  * The weights are taken against a reference maximum that is raised only
+//    when a tile's maximum exceeds it by more than kLazy (base 2; the identity holds
+//    for any constant), so o is almost never rescaled inside the loop; the true
+//    running maximum is tracked alongside and (l, o) are brought to it before
+//    they are stored.
 //  * Workgroup ids are remapped so that consecutive query tiles of one
 //    (batch, head, resident block) -- which read the same K/V -- land on the
 //    same XCD and share its L2.
@@ -46,10 +53,10 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 4;
-constexpr int kTileQ = kWaves * 32;  // query rows per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+// Lazy rescaling threshold (base-2 units): weights stay below 2^kLazy.
+constexpr float kLazy = 8.0f;
 
 // Workgroups are dispatched round-robin over the 8 XCDs.  Return the logical
 // tile id such that each XCD walks a contiguous range of logical tiles.
@@ -112,21 +119,43 @@ __device__ __forceinline__ void gload_lds16(const __bf16* g, __bf16* lds_wave_ba
                                    (__attribute__((address_space(3))) void*)(lds_wave_base), 16, 0, 0);
 }
 
+// Buffer resource over `base` with no effective range limit (every access is
+// computed in bounds by the kernel) for the raw buffer loads below.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
+}
+
+// 16 bytes at byte offset voff of the buffer straight into LDS
+// (buffer_load_dwordx4 ... lds): lane i's bytes land at lds_wave_base + 16 i.
+// The 64-bit base lives in scalar registers, so a tile costs no vector
+// address arithmetic.
+__device__ __forceinline__ void bload_lds16(__amdgpu_buffer_rsrc_t rs, int voff, __bf16* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(lds_wave_base), 16, voff, 0,
+                                           0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Per tile: wait for it, request the next one into the other buffer, scores,
+// maximum tracking, bf16 weights and their sum, value product.  Full tiles run
+// in a loop unrolled by two, so both LDS buffers have compile-time offsets; a
+// ragged last tile runs once after it, with key masking.  The per-wave state
+// is written for G groups of 32 query rows; one group per wave is used.
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1 : 2)))
 void fold_bf16_kernel(const FoldParams p) {
+  constexpr int G = 1;  // query groups of 32 rows per wave
   constexpr int TK = TileCfg<D>::TK;
-  constexpr int NKB = TK / 32;          // 32-key blocks per tile
-  constexpr int NC = D / 16;            // 16-wide d chunks of the score contraction
-  constexpr int NDB = D / 32;           // 32-wide d blocks of the output
-  constexpr int UPR = D / 8;            // 16-byte units per K/V row
-  constexpr int TE = TK * D;            // elements of one K (or V) tile
-  constexpr int CPW = TE / 512 / 4;     // 1 KB direct-load chunks per wave per tensor
+  constexpr int NKB = TK / 32;
+  constexpr int NC = D / 16;
+  constexpr int NDB = D / 32;
+  constexpr int UPR = D / 8;
+  constexpr int TE = TK * D;
+  constexpr int CPW = TE / 512 / 4;
+  constexpr int QT = 4 * 32 * G;  // query rows per workgroup
   static_assert(CPW >= 1 && TE % 2048 == 0, "tile must split into whole 1 KB chunks per wave");
-  // Two buffers, each a K tile followed by a V tile, rows unpadded, units swizzled.
   __shared__ __attribute__((aligned(1024))) __bf16 lds[2 * 2 * TE];
 
-  const int tiles_q = (p.q_rows + kTileQ - 1) / kTileQ;
+  const int tiles_q = (p.q_rows + QT - 1) / QT;
   const int total = tiles_q * p.n_res * p.H * p.B;
   int w = xcd_remap(blockIdx.x, total);
   const int qt = w % tiles_q;
@@ -142,76 +171,84 @@ void fold_bf16_kernel(const FoldParams p) {
   const int lr = lane & 31;
   const int lg = lane >> 5;
 
-  const int row = qt * kTileQ + wave * 32 + lr;
-  const bool row_ok = row < p.q_rows;
-  const int64_t srow = (int64_t)r * p.q_rows + (row_ok ? row : p.q_rows - 1);
-
-  // Q fragments: B operand of S^T = K Q^T; lane holds Q[row][16c + 8lg .. +8].
-  bf16x8 qf[NC];
-  {
-    const __bf16* qp = (const __bf16*)p.q + bi * p.q_sb + hi * p.q_sh + srow * p.q_sr + 8 * lg;
+  int64_t srow[G], st_row[G];
+  bool row_ok[G];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) qf[c] = *(const bf16x8*)(qp + 16 * c);
+  for (int g = 0; g < G; ++g) {
+    const int row = qt * QT + wave * 32 * G + g * 32 + lr;
+    row_ok[g] = row < p.q_rows;
+    srow[g] = (int64_t)r * p.q_rows + (row_ok[g] ? row : p.q_rows - 1);
+    st_row[g] = ((int64_t)bi * p.H + hi) * p.st_bh + srow[g];
   }
 
-  // Running state.  O^T accumulator layout: oacc[db][4j + e] holds
-  // o[row][32 db + 8 j + 4 lg + e].  l is kept as two partial sums, one per
-  // lane half, added at the end.
-  const int64_t st_row = ((int64_t)bi * p.H + hi) * p.st_bh + srow;
-  float mc;  // running max in base-2 units of the scaled score
-  float lpart;
-  f32x16 oacc[NDB];
-  if (p.flags & kLoadState) {
-    mc = p.m[st_row] * kLog2e;
-    lpart = lg == 0 ? p.l[st_row] : 0.0f;
-    const float* orow = p.o + st_row * D + 4 * lg;
+  bf16x8 qf[G][NC];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+  for (int g = 0; g < G; ++g) {
+    const __bf16* qp = (const __bf16*)p.q + bi * p.q_sb + hi * p.q_sh + srow[g] * p.q_sr + 8 * lg;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 t = *(const f32x4*)(orow + 32 * db + 8 * j);
+    for (int c = 0; c < NC; ++c) qf[g][c] = *(const bf16x8*)(qp + 16 * c);
+  }
+
+  // mref: the reference maximum the weights are taken against (base-2 units
+  // of the scaled score); it trails the true running maximum mtrue by less
+  // than kLazy, which keeps every weight below 2^kLazy.  o and l are rescaled
+  // to mtrue once, before they are stored.
+  float mref[G], mtrue[G], lpart[G];
+  f32x16 oacc[G][NDB];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) oacc[db][4 * j + e] = t[e];
-      }
-  } else {
-    mc = -INFINITY;
-    lpart = 0.0f;
+  for (int g = 0; g < G; ++g) {
+    if (p.flags & kLoadState) {
+      mref[g] = p.m[st_row[g]] * kLog2e;
+      lpart[g] = lg == 0 ? p.l[st_row[g]] : 0.0f;
+      const float* orow = p.o + st_row[g] * D + 4 * lg;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[db][i] = 0.0f;
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 t = *(const f32x4*)(orow + 32 * db + 8 * j);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) oacc[g][db][4 * j + e] = t[e];
+        }
+    } else {
+      mref[g] = -INFINITY;
+      lpart[g] = 0.0f;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[g][db][i] = 0.0f;
+    }
+    mtrue[g] = mref[g];
   }
 
   const __bf16* kbase = (const __bf16*)p.k + bi * p.k_sb + hi * p.k_sh + p.k_off[r];
   const __bf16* vbase = (const __bf16*)p.v + bi * p.v_sb + hi * p.v_sh + p.v_off[r];
+  const int n_full = p.kv_rows / TK;
   const int n_kt = (p.kv_rows + TK - 1) / TK;
   const float c2 = p.scale_log2;
 
-  // Direct-load addressing: chunk c of a tile is LDS units [64c, 64c + 64);
-  // lane i writes unit 64c + i = (row, pos) and so fetches global unit
-  // pos ^ swz(row) of that row.
-  // (The host guarantees row strides below 2^24 elements, so these fit in 32 bits.)
+  // Direct loads: chunk c of a tile is LDS units [64c, 64c + 64); lane i
+  // writes unit 64c + i = (row, pos) and fetches global unit pos ^ swz(row).
   const int k_sr = (int)p.k_sr, v_sr = (int)p.v_sr;
-  int ld_koff[CPW], ld_voff[CPW];
+  int ld_koff[CPW], ld_voff[CPW];  // byte offsets inside a tile
 #pragma unroll
   for (int j = 0; j < CPW; ++j) {
     const int u = (wave * CPW + j) * 64 + lane;
     const int lrow = u / UPR;
     const int gunit = (u % UPR) ^ swz<D>(lrow);
-    ld_koff[j] = lrow * k_sr + gunit * 8;
-    ld_voff[j] = lrow * v_sr + gunit * 8;
+    ld_koff[j] = (lrow * k_sr + gunit * 8) * 2;
+    ld_voff[j] = (lrow * v_sr + gunit * 8) * 2;
   }
   auto issue_tile = [&](int kt, int buf) {
     const int key0 = kt * TK;
     __bf16* kl = lds + buf * 2 * TE + wave * CPW * 512;
     __bf16* vl = kl + TE;
     if (key0 + TK <= p.kv_rows) {
-      const __bf16* kg = kbase + (int64_t)key0 * k_sr;
-      const __bf16* vg = vbase + (int64_t)key0 * v_sr;
+      const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + (int64_t)key0 * k_sr);
+      const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + (int64_t)key0 * v_sr);
 #pragma unroll
       for (int j = 0; j < CPW; ++j) {
-        gload_lds16(kg + ld_koff[j], kl + j * 512);
-        gload_lds16(vg + ld_voff[j], vl + j * 512);
+        bload_lds16(kr, ld_koff[j], kl + j * 512);
+        bload_lds16(vr, ld_voff[j], vl + j * 512);
       }
     } else {  // ragged last tile: rows past the end re-read the last row
 #pragma unroll
@@ -226,14 +263,10 @@ void fold_bf16_kernel(const FoldParams p) {
     }
   };
 
-  // LDS read addressing (element offsets inside a K or V tile).
-  // K (A operand of S^T): row 32kb + lr, unit 2c + lg  -> ((2c) ^ gk) with gk = lg ^ swz(lr).
   const int gk = lg ^ swz<D>(lr);
   int k_rd[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) k_rd[c] = lr * D + (((2 * c) ^ gk) << 3);
-  // V (A operand of O^T, transposed reads): row 32kb + 16c + vr (+8), column
-  // 32db + 16h + 4(lane & 3), i.e. unit (4db + x) with x = 2h + ((lane & 3) >> 1).
   const int vr = 4 * lg + ((lane & 15) >> 2);
   const int vx = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
   int v_rd[2][NDB];
@@ -245,77 +278,69 @@ void fold_bf16_kernel(const FoldParams p) {
     for (int db = 0; db < NDB; ++db) v_rd[run][db] = rr * D + (((4 * db) ^ y) << 3) + 4 * (lane & 1);
   }
 
-  if (n_kt > 0) issue_tile(0, 0);
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int buf = kt & 1;
-    const int key0 = kt * TK;
-    // Tile kt landed (this wave's loads), then every wave's loads and every
-    // wave's reads of the other buffer (previous iteration) are complete.
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    __syncthreads();
-    if (kt + 1 < n_kt) issue_tile(kt + 1, buf ^ 1);
-    const __bf16* kl = lds + buf * 2 * TE;
-    const __bf16* vl = kl + TE;
-
-    // S^T for the 32-key blocks: sacc[kb][i] is the score of query row `row`
-    // against key key0 + 32 kb + 8 (i / 4) + 4 lg + i % 4.
-    f32x16 sacc[NKB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.0f;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const bf16x8 a = *(const bf16x8*)(kl + 32 * kb * D + k_rd[c]);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], sacc[kb], 0, 0, 0);
-      }
-    }
-    if (key0 + TK > p.kv_rows) {  // ragged last tile: keys past the end get -inf
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = key0 + 32 * kb + 8 * (i >> 2) + 4 * lg + (i & 3);
-          if (key >= p.kv_rows) sacc[kb][i] = -INFINITY;
-        }
-    }
-
-    float mx = sacc[0][0];
+  // S^T of group g against the K tile at kl; the 32-key blocks are
+  // independent accumulation chains, interleaved.
+  auto scores = [&](f32x16 (&s)[NKB], const __bf16* kl, int g) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-    mx = pair_max(mx);
-    // Every tile holds at least one real key, so mx and m_new are finite and
-    // alpha = exp2(-inf) = 0 on the first tile of a fresh state.
-    const float m_new = fmaxf(mc, mx * c2);
-    const float alpha = __builtin_amdgcn_exp2f(mc - m_new);
-    mc = m_new;
-
-    unsigned pk[NKB][8];
+      for (int i = 0; i < 16; ++i) s[kb][i] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const bf16x8 a = *(const bf16x8*)(kl + 32 * kb * D + k_rd[c]);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[g][c], s[kb], 0, 0, 0);
+      }
+  };
+  auto mask = [&](f32x16 (&s)[NKB], int key0) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (key0 + 32 * kb + 8 * (i >> 2) + 4 * lg + (i & 3) >= p.kv_rows) s[kb][i] = -INFINITY;
+  };
+  // Row maximum of the tile; raises mtrue, and mref when it falls more than
+  // kLazy below the new maximum (rare: then o and l are rescaled here).  A
+  // row that has seen no key yet (mref = -inf, o = 0, l = 0) just takes the
+  // new maximum as its reference.
+  auto track_max = [&](const f32x16 (&s)[NKB], int g) {
+    float mx = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+    const float mt = pair_max(mx) * c2;
+    mtrue[g] = fmaxf(mtrue[g], mt);
+    const bool fresh = mref[g] == -INFINITY;
+    const bool raise = !fresh && mt > mref[g] + kLazy;
+    if (fresh) mref[g] = mt;
+    if (__builtin_amdgcn_ballot_w64(raise)) {
+      const float alpha = raise ? __builtin_amdgcn_exp2f(mref[g] - mt) : 1.0f;
+      if (raise) mref[g] = mt;
+      lpart[g] *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[g][db][i] *= alpha;
+    }
+  };
+  // bf16 weights exp2(s c - mref) as packed pairs, and their sum into l.
+  auto weights = [&](const f32x16 (&s)[NKB], unsigned (&pk)[NKB][8], int g) {
+    const float mr = mref[g];
     float lsum = 0.0f;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][2 * j], c2, -m_new));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][2 * j + 1], c2, -m_new));
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][2 * j], c2, -mr));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][2 * j + 1], c2, -mr));
         pk[kb][j] = pack_bf16(p0, p1);
         lsum = sum_bf16_pair(pk[kb][j], lsum);
       }
-    lpart = fmaf(lpart, alpha, lsum);
-    // o is rescaled only when some row of this wave raised its maximum
-    // (alpha == 1 exactly otherwise).
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-    }
-
-    // O^T += V^T P^T.  For key chunk (kb, c) the lane's B operand is its
-    // weights i = 8c .. 8c+7 of block kb, i.e. keys 32kb+16c+4lg+{0..3} and
-    // 32kb+16c+8+4lg+{0..3}; the A operand holds V at the same keys, column d.
+    lpart[g] += lsum;
+  };
+  auto values = [&](const unsigned (&pk)[NKB][8], const __bf16* vl, int g) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -330,60 +355,97 @@ void fold_bf16_kernel(const FoldParams p) {
           const u32x2 w0 = __builtin_bit_cast(u32x2, t0);
           const u32x2 w1 = __builtin_bit_cast(u32x2, t1);
           const u32x4 aw = {w0[0], w0[1], w1[0], w1[1]};
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, aw), b, oacc[db], 0, 0, 0);
+          oacc[g][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, aw), b, oacc[g][db], 0, 0, 0);
         }
       }
+  };
+
+  // One tile whose K/V sit in LDS buffer `buf`; `ragged` masks keys past the end.
+  auto tile = [&](int kt, int buf, bool ragged) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile kt landed for this wave
+    __syncthreads();                     // ... for every wave; the other buffer is free
+    if (kt + 1 < n_kt) issue_tile(kt + 1, buf ^ 1);
+    const __bf16* kc = lds + buf * 2 * TE;
+    const __bf16* vc = kc + TE;
+    f32x16 sa[NKB];
+    unsigned pa[NKB][8];
+    scores(sa, kc, 0);
+    if (ragged) mask(sa, kt * TK);
+    track_max(sa, 0);
+    weights(sa, pa, 0);
+    values(pa, vc, 0);
+  };
+
+  if (n_kt > 0) {
+    issue_tile(0, 0);
+    int kt = 0;
+    for (; kt + 2 <= n_full; kt += 2) {
+      tile(kt, 0, false);
+      tile(kt + 1, 1, false);
+    }
+    if (kt < n_full) {
+      tile(kt, 0, false);
+      ++kt;
+    }
+    if (kt < n_kt) tile(kt, kt & 1, true);
   }
 
-  const float l_tot = pair_sum(lpart);
-  if (!row_ok) return;
-  if (p.flags & kWriteOut) {
-    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    __bf16* orow = (__bf16*)p.out + bi * p.out_sb + hi * p.out_sh + srow * p.out_sr + 4 * lg;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+  for (int g = 0; g < G; ++g) {
+    // Bring (l, o) from the reference maximum to the true running maximum.
+    const float fix = mref[g] == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(mref[g] - mtrue[g]);
+    const float l_tot = pair_sum(lpart[g]) * fix;
+    if (!row_ok[g]) continue;
+    if (p.flags & kWriteOut) {
+      const float inv = l_tot > 0.0f ? fix / l_tot : 0.0f;
+      __bf16* orow = (__bf16*)p.out + bi * p.out_sb + hi * p.out_sh + srow[g] * p.out_sr + 4 * lg;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        bf16x4 t;
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) t[e] = (__bf16)(oacc[db][4 * j + e] * inv);
-        *(bf16x4*)(orow + 32 * db + 8 * j) = t;
-      }
-  }
-  if (p.flags & kStoreState) {
-    if (lg == 0) {
-      p.m[st_row] = mc * kLn2;
-      p.l[st_row] = l_tot;
+        for (int j = 0; j < 4; ++j) {
+          bf16x4 t;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) t[e] = (__bf16)(oacc[g][db][4 * j + e] * inv);
+          *(bf16x4*)(orow + 32 * db + 8 * j) = t;
+        }
     }
-    float* orow = p.o + st_row * D + 4 * lg;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        f32x4 t;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) t[e] = oacc[db][4 * j + e];
-        *(f32x4*)(orow + 32 * db + 8 * j) = t;
+    if (p.flags & kStoreState) {
+      if (lg == 0) {
+        p.m[st_row[g]] = mtrue[g] * kLn2;
+        p.l[st_row[g]] = l_tot;
       }
+      float* orow = p.o + st_row[g] * D + 4 * lg;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          f32x4 t;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) t[e] = oacc[g][db][4 * j + e] * fix;
+          *(f32x4*)(orow + 32 * db + 8 * j) = t;
+        }
+    }
   }
 }
 
 }  // namespace
 
 hipError_t launch_fold_bf16(const FoldParams& p, int d, hipStream_t s) {
-  const int64_t tiles_q = (p.q_rows + kTileQ - 1) / kTileQ;
+  constexpr int rows_per_wg = 4 * 32;
+  const int64_t tiles_q = (p.q_rows + rows_per_wg - 1) / rows_per_wg;
   const int64_t grid = tiles_q * p.n_res * p.H * p.B;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  const dim3 gd((unsigned)grid), bd(256);
   switch (d) {
     case 64:
-      fold_bf16_kernel<64><<<dim3((unsigned)grid), dim3(256), 0, s>>>(p);
+      fold_bf16_kernel<64><<<gd, bd, 0, s>>>(p);
       break;
     case 128:
-      fold_bf16_kernel<128><<<dim3((unsigned)grid), dim3(256), 0, s>>>(p);
+      fold_bf16_kernel<128><<<gd, bd, 0, s>>>(p);
       break;
     case 256:
-      fold_bf16_kernel<256><<<dim3((unsigned)grid), dim3(256), 0, s>>>(p);
+      fold_bf16_kernel<256><<<gd, bd, 0, s>>>(p);
       break;
     default:
       return hipErrorInvalidValue;

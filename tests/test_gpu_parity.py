@@ -110,6 +110,38 @@ def test_fold_block_state_per_step(ra, dtype, d, q_rows, kv_rows):
         check_output(to64(o) / to64(l)[..., None], r.o / r.l[..., None], dtype, f"step {t} o/l")
 
 
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_fold_block_large_max_jumps(ra, d):
+    """Scores whose running maximum jumps far (hundreds of base-2 units) inside
+    one block and across blocks, and rows whose maximum comes first: the
+    reference-maximum bookkeeping must rescale exactly when needed."""
+    _say(f"fold_block large maximum jumps d={d}")
+    B, H, q_rows, kv_rows = 1, 2, 160, 300
+    gen = torch.Generator(device="cuda").manual_seed(99 + d)
+    q = torch.randn((B, H, q_rows, d), generator=gen, device="cuda")
+    ks, vs = [], []
+    for t in range(3):
+        k = torch.randn((B, H, kv_rows, d), generator=gen, device="cuda")
+        # key rows grow in magnitude along the block (later tiles dominate),
+        # and a few rows of q see their largest scores in the first tile
+        k = k * torch.linspace(0.5, 6.0 + 4 * t, kv_rows, device="cuda")[None, None, :, None]
+        k[:, :, :8] *= 12.0
+        ks.append(k.bfloat16())
+        vs.append(torch.randn((B, H, kv_rows, d), generator=gen, device="cuda").bfloat16())
+    q = q.bfloat16()
+    m, l, o = _new_state(B, H, q_rows, d)
+    ra.ra_state_init(m, l, o)
+    ref = _oracle_steps(q, ks, vs)
+    for t in range(3):
+        ra.ra_fold_block(q, ks[t], vs[t], m, l, o)
+        torch.cuda.synchronize()
+        r = ref[t]
+        np.testing.assert_allclose(to64(m), r.m, rtol=1e-5, atol=1e-3)
+        assert np.all(np.isfinite(to64(l))) and np.all(np.isfinite(to64(o)))
+        np.testing.assert_allclose(to64(l), r.l, rtol=1e-2)
+        check_output(to64(o) / to64(l)[..., None], r.o / r.l[..., None], "bf16", f"step {t} o/l")
+
+
 def test_fold_block_zero_rows_is_noop(ra):
     _say("fold_block kv_rows=0 / q_rows=0")
     q = torch.randn((1, 1, 64, 128), device="cuda").bfloat16()
