@@ -18,6 +18,9 @@ Everything here is plain NumPy in float64, written from the pages:
   (i - t) mod P, finished with o / l (math page, "The ring schedule" and
   "Accumulation math, step by step").
 * ``ring_schedule`` -- the block a device holds at each step.
+* ``layouts`` -- contiguous, striped and zig-zag token layouts and the causal
+  positions they imply (math page "Causal masking, load balance, and other
+  wrinkles"; vibeengines.com "The causal-mask catch").
 
 Every function here is pinned by ``tests/test_oracle.py`` against values the
 pages print (the worked two-block example), closed forms, a brute-force
@@ -25,6 +28,7 @@ pure-Python evaluation, a library routine (torch's fp64 CPU attention) and
 invariants the pages state (order independence, P = 1).
 """
 
+from . import layouts
 from .attention import dense_attention, dense_attention_rows
 from .ring import (
     State,
@@ -37,6 +41,7 @@ from .ring import (
 
 __all__ = [
     "State",
+    "layouts",
     "dense_attention",
     "dense_attention_rows",
     "finalize",

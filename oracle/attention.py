@@ -29,7 +29,8 @@ def _as_f64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
 
 
-def dense_attention(q, k, v, scale: float | None = None, row_chunk: int = 1024) -> np.ndarray:
+def dense_attention(q, k, v, scale: float | None = None, row_chunk: int = 1024, q_pos=None,
+                    k_pos=None) -> np.ndarray:
     """O = softmax(Q K^T * scale) V for every leading (batch, head) index.
 
     q: [..., Nq, d], k: [..., Nk, d], v: [..., Nk, dv] (leading dims equal).
@@ -38,6 +39,11 @@ def dense_attention(q, k, v, scale: float | None = None, row_chunk: int = 1024) 
     ratio; it only keeps exp in range.  Computed in float64, ``row_chunk``
     query rows at a time so memory stays bounded; chunking rows does not change
     any row's arithmetic.
+
+    With ``q_pos`` [Nq] and ``k_pos`` [Nk] (sequence positions) the attention
+    is causal: a query sees only keys at or before its own position (math
+    page, "Causal masking, load balance, and other wrinkles").  A row that sees
+    no key at all gives 0.
     """
     q = _as_f64(q)
     k = _as_f64(k)
@@ -48,9 +54,20 @@ def dense_attention(q, k, v, scale: float | None = None, row_chunk: int = 1024) 
     nq = q.shape[-2]
     out = np.empty(q.shape[:-1] + (v.shape[-1],), dtype=np.float64)
     kt = np.swapaxes(k, -1, -2)
+    causal = q_pos is not None
+    if causal:
+        q_pos = np.asarray(q_pos)
+        k_pos = np.asarray(k_pos)
     for r0 in range(0, nq, row_chunk):
         r1 = min(nq, r0 + row_chunk)
         s = np.matmul(q[..., r0:r1, :], kt) * scale  # [..., rows, Nk]
+        if causal:
+            s = np.where(k_pos[None, :] > q_pos[r0:r1, None], -np.inf, s)
+            mx = s.max(axis=-1, keepdims=True)
+            p = np.exp(s - np.where(np.isneginf(mx), 0.0, mx))
+            z = p.sum(axis=-1, keepdims=True)
+            out[..., r0:r1, :] = np.matmul(p, v) / np.where(z > 0, z, 1.0)
+            continue
         s = s - s.max(axis=-1, keepdims=True)
         p = np.exp(s)
         out[..., r0:r1, :] = np.matmul(p, v) / p.sum(axis=-1, keepdims=True)

@@ -66,21 +66,28 @@ def fold_scores(state: State, s: np.ndarray, v_blk: np.ndarray) -> State:
     if s.shape[-1] == 0:
         return state.copy()
     m_new = np.maximum(state.m, s.max(axis=-1))
-    alpha = np.exp(state.m - m_new)  # exp(-inf) = 0 on the first block
-    p = np.exp(s - m_new[..., None])
+    # A row that has still seen no visible key (every score so far -inf, only
+    # possible under a causal mask) keeps its state: alpha = 1, weights 0.
+    none = np.isneginf(m_new)
+    m_safe = np.where(none, 0.0, m_new)
+    alpha = np.where(none, 1.0, np.exp(state.m - m_safe))  # exp(-inf) = 0 on the first block
+    p = np.exp(s - m_safe[..., None])
     l_new = alpha * state.l + p.sum(axis=-1)
     o_new = alpha[..., None] * state.o + np.matmul(p, v_blk)
     return State(m_new, l_new, o_new)
 
 
-def fold(state: State, q_blk, k_blk, v_blk, scale: float | None = None) -> State:
-    """S = Q_i K_blk^T / sqrt(d), then ``fold_scores`` (math page loop body)."""
+def fold(state: State, q_blk, k_blk, v_blk, scale: float | None = None, q_pos=None, k_pos=None) -> State:
+    """S = Q_i K_blk^T / sqrt(d), then ``fold_scores`` (math page loop body).
+    With positions, keys after a query's position are masked to -inf (causal)."""
     q_blk = _as_f64(q_blk)
     k_blk = _as_f64(k_blk)
     v_blk = _as_f64(v_blk)
     if scale is None:
         scale = 1.0 / math.sqrt(q_blk.shape[-1])
     s = np.matmul(q_blk, np.swapaxes(k_blk, -1, -2)) * scale
+    if q_pos is not None:
+        s = np.where(np.asarray(k_pos)[None, :] > np.asarray(q_pos)[:, None], -np.inf, s)
     return fold_scores(state, s, v_blk)
 
 
@@ -107,6 +114,7 @@ def ring_attention(
     scale: float | None = None,
     order: Callable[[int], Sequence[int]] | None = None,
     return_states: bool = False,
+    causal_layout: str | None = None,
 ):
     """Run the per-device loop for each resident query block.
 
@@ -116,6 +124,9 @@ def ring_attention(
       (default: the ring schedule (i - t) mod P).  The math page's worked
       example and vibeengines.com method step 4 say the result does not depend
       on the order; tests use other orders to check exactly that.
+    causal_layout: None for full attention, or "contiguous", "striped" or
+      "zigzag": then q, k, v are in that layout's device order (see
+      ``oracle.layouts``) and a query sees only keys at or before its position.
     Returns O for the resident blocks stacked along the row axis
     ([..., len(query_blocks) * b, dv]); with ``return_states`` also the list,
     per resident block, of the state after every step.
@@ -133,6 +144,11 @@ def ring_attention(
         order = lambda i: ring_schedule(P, i)  # noqa: E731
     lead = q.shape[:-2]
     dv = v.shape[-1]
+    pos = None
+    if causal_layout is not None:
+        from .layouts import positions
+
+        pos = positions(causal_layout, P, b)
     outs = []
     all_states = []
     for i in query_blocks:
@@ -140,7 +156,8 @@ def ring_attention(
         state = init_state(lead, b, dv)
         states = []
         for j in order(i):
-            state = fold(state, q_i, k[..., j * b:(j + 1) * b, :], v[..., j * b:(j + 1) * b, :], scale)
+            qp, kp = (None, None) if pos is None else (pos[i], pos[j])
+            state = fold(state, q_i, k[..., j * b:(j + 1) * b, :], v[..., j * b:(j + 1) * b, :], scale, qp, kp)
             states.append(state.copy())
         outs.append(finalize(state))
         all_states.append(states)
