@@ -8,10 +8,13 @@ include/ra.h); this package is its thin ctypes binding:
 * ``ra_finalize``    -- O = o / l
 * ``ra_ring_forward`` -- all P virtual ring steps for the resident query blocks,
   with the double-buffered K/V hand-off on a side stream
+* ``ra_fold_block_causal``, ``ra_ring_forward_causal`` -- the same under a
+  causal mask, for contiguous, striped or zig-zag token layouts
 * ``ra_ring_workspace_bytes``, ``ra_last_error``, ``ra_version``
 """
 
 from .binding import (
+    CAUSAL_LAYOUTS,
     EXPORTED,
     RA_DTYPE_BF16,
     RA_DTYPE_F32,
@@ -20,16 +23,19 @@ from .binding import (
     load,
     ra_finalize,
     ra_fold_block,
+    ra_fold_block_causal,
     ra_profile_folds,
     ra_profile_read,
     ra_last_error,
     ra_ring_forward,
+    ra_ring_forward_causal,
     ra_ring_workspace_bytes,
     ra_state_init,
     ra_version,
 )
 
 __all__ = [
+    "CAUSAL_LAYOUTS",
     "EXPORTED",
     "RA_DTYPE_BF16",
     "RA_DTYPE_F32",
@@ -38,10 +44,12 @@ __all__ = [
     "load",
     "ra_finalize",
     "ra_fold_block",
+    "ra_fold_block_causal",
     "ra_profile_folds",
     "ra_profile_read",
     "ra_last_error",
     "ra_ring_forward",
+    "ra_ring_forward_causal",
     "ra_ring_workspace_bytes",
     "ra_state_init",
     "ra_version",

@@ -22,14 +22,24 @@ RA_E_HIP = 3
 RA_E_OOM = 4
 RA_DTYPE_F32 = 0
 RA_DTYPE_BF16 = 1
+RA_CAUSAL_NONE = 0
+RA_CAUSAL_CONTIGUOUS = 1
+RA_CAUSAL_STRIPED = 2
+RA_CAUSAL_ZIGZAG = 3
+
+#: token layouts of a causal ring by name (None: full attention)
+CAUSAL_LAYOUTS = {None: RA_CAUSAL_NONE, "contiguous": RA_CAUSAL_CONTIGUOUS, "striped": RA_CAUSAL_STRIPED,
+                  "zigzag": RA_CAUSAL_ZIGZAG}
 
 #: every symbol include/ra.h declares
 EXPORTED = (
     "ra_state_init",
     "ra_fold_block",
+    "ra_fold_block_causal",
     "ra_finalize",
     "ra_ring_workspace_bytes",
     "ra_ring_forward",
+    "ra_ring_forward_causal",
     "ra_last_error",
     "ra_version",
     "ra_profile_folds",
@@ -69,6 +79,9 @@ def load() -> ctypes.CDLL:
     lib.ra_fold_block.argtypes = [vp, strides, vp, strides, vp, strides, ctypes.c_int, i64, i64, i64, i64, i64, f32,
                                   vp, vp, vp, vp]
     lib.ra_fold_block.restype = ctypes.c_int
+    lib.ra_fold_block_causal.argtypes = [vp, strides, vp, strides, vp, strides, ctypes.c_int, i64, i64, i64, i64,
+                                         f32, ctypes.c_int, i32, i32, i32, vp, vp, vp, vp]
+    lib.ra_fold_block_causal.restype = ctypes.c_int
     lib.ra_finalize.argtypes = [vp, vp, vp, strides, ctypes.c_int, i64, i64, i64, i64, vp]
     lib.ra_finalize.restype = ctypes.c_int
     lib.ra_ring_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i64, i64, i32, i32]
@@ -76,6 +89,10 @@ def load() -> ctypes.CDLL:
     lib.ra_ring_forward.argtypes = [vp, strides, vp, strides, vp, strides, vp, strides, ctypes.c_int, i64, i64, i64,
                                     i64, i32, ctypes.POINTER(ctypes.c_int32), i32, f32, vp, sz, vp]
     lib.ra_ring_forward.restype = ctypes.c_int
+    lib.ra_ring_forward_causal.argtypes = [vp, strides, vp, strides, vp, strides, vp, strides, ctypes.c_int, i64,
+                                           i64, i64, i64, i32, ctypes.POINTER(ctypes.c_int32), i32, f32,
+                                           ctypes.c_int, vp, sz, vp]
+    lib.ra_ring_forward_causal.restype = ctypes.c_int
     lib.ra_last_error.argtypes = []
     lib.ra_last_error.restype = ctypes.c_char_p
     lib.ra_version.argtypes = []
@@ -173,6 +190,34 @@ def ra_fold_block(q, k, v, m, l, o, scale: float = 0.0, stream=None) -> None:
         B, H, q_rows, kv_rows, d, float(scale), _dev(m, "m"), _dev(l, "l"), _dev(o, "o"), _stream(stream)))
 
 
+def _layout_code(layout) -> int:
+    if isinstance(layout, int):
+        return layout
+    if layout not in CAUSAL_LAYOUTS:
+        raise ValueError(f"unknown causal layout {layout!r}: use one of {sorted(k for k in CAUSAL_LAYOUTS if k)}")
+    return CAUSAL_LAYOUTS[layout]
+
+
+def ra_fold_block_causal(q, k, v, m, l, o, layout, P: int, q_block: int, kv_block: int, scale: float = 0.0,
+                         stream=None) -> None:
+    """Fold device kv_block's block into device q_block's state under the causal
+    mask of a P-device ring in ``layout`` ("contiguous", "striped", "zigzag");
+    q, k, v: [B, H, b, d]."""
+    _state_ok(m, l, o)
+    B, H, rows, d = q.shape
+    if k.shape != v.shape or k.shape != q.shape:
+        raise ValueError(f"q, k and v must share one [B, H, b, d] shape: {tuple(q.shape)}, {tuple(k.shape)}, "
+                         f"{tuple(v.shape)}")
+    if tuple(o.shape) != (B, H, rows, d) or tuple(m.shape) != (B, H, rows) or tuple(l.shape) != (B, H, rows):
+        raise ValueError("state shapes do not match q")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must have one dtype")
+    _check(load().ra_fold_block_causal(
+        _dev(q, "q"), _strides(q), _dev(k, "k"), _strides(k), _dev(v, "v"), _strides(v), _dtype_code(q),
+        B, H, rows, d, float(scale), _layout_code(layout), int(P), int(q_block), int(kv_block),
+        _dev(m, "m"), _dev(l, "l"), _dev(o, "o"), _stream(stream)))
+
+
 def ra_finalize(l, o, out, stream=None) -> None:
     """out = o / l (0 where l == 0), cast to out's dtype."""
     B, H, rows, d = o.shape
@@ -190,6 +235,16 @@ def ra_ring_workspace_bytes(dtype, B: int, H: int, N: int, d: int, P: int, n_q: 
 def ra_ring_forward(q, k, v, P: int, query_blocks: Sequence[int] | None = None, out=None, scale: float = 0.0,
                     workspace=None, stream=None):
     """The whole ring for the resident query blocks; returns out ([B, H, n_q*b, d])."""
+    return _ring(q, k, v, P, query_blocks, out, scale, workspace, stream, None)
+
+
+def ra_ring_forward_causal(q, k, v, P: int, layout, query_blocks: Sequence[int] | None = None, out=None,
+                           scale: float = 0.0, workspace=None, stream=None):
+    """The causal ring: q, k, v in ``layout``'s device order; returns out."""
+    return _ring(q, k, v, P, query_blocks, out, scale, workspace, stream, layout)
+
+
+def _ring(q, k, v, P, query_blocks, out, scale, workspace, stream, layout):
     import torch
 
     B, H, N, d = k.shape
@@ -210,10 +265,12 @@ def ra_ring_forward(q, k, v, P: int, query_blocks: Sequence[int] | None = None, 
         ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
     if not (q.dtype == k.dtype == v.dtype == out.dtype):
         raise TypeError("q, k, v and out must have one dtype")
-    _check(load().ra_ring_forward(
-        _dev(q, "q"), _strides(q), _dev(k, "k"), _strides(k), _dev(v, "v"), _strides(v), _dev(out, "out"),
-        _strides(out), _dtype_code(q), B, H, N, d, int(P), qb, n_q, float(scale), ws_ptr, ws_bytes,
-        _stream(stream)))
+    args = (_dev(q, "q"), _strides(q), _dev(k, "k"), _strides(k), _dev(v, "v"), _strides(v), _dev(out, "out"),
+            _strides(out), _dtype_code(q), B, H, N, d, int(P), qb, n_q, float(scale))
+    if layout is None:
+        _check(load().ra_ring_forward(*args, ws_ptr, ws_bytes, _stream(stream)))
+    else:
+        _check(load().ra_ring_forward_causal(*args, _layout_code(layout), ws_ptr, ws_bytes, _stream(stream)))
     return out
 
 

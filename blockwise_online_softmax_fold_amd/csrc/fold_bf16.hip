@@ -37,6 +37,12 @@
 //  * Workgroup ids are remapped so that consecutive query tiles of one
 //    (batch, head, resident block) -- which read the same K/V -- land on the
 //    same XCD and share its L2.
+//  * Causal masking (math page, "Causal masking, load balance, and other
+//    wrinkles"): positions rise with the row index in every token layout, so
+//    the keys a query tile can see are a prefix of the visiting block.  Tiles
+//    past that prefix are never loaded, tiles every row of the workgroup sees
+//    run unmasked, and only the few tiles in between compare each key with the
+//    row's last visible key.
 #include <math.h>
 
 #include "kernels.h"
@@ -171,6 +177,21 @@ void fold_bf16_kernel(const FoldParams p) {
   const int lr = lane & 31;
   const int lg = lane >> 5;
 
+  // Keys [0, kv_vis) are visible to some row of this workgroup, keys
+  // [0, kv_all) to every row; key c is visible to this lane's row iff c <= lim.
+  int kv_vis = p.kv_rows, kv_all = p.kv_rows;
+  int lim = p.kv_rows - 1;
+  if (p.mask != kMaskNone) {
+    const int qb = p.q_blk[r], kb = p.kv_blk[r];
+    const int q_first = qt * QT, q_last = min(q_first + QT, p.q_rows) - 1;
+    kv_vis = last_key_at_or_before(p.mask, p.P, p.blk, kb, token_pos(p.mask, p.P, p.blk, qb, q_last)) + 1;
+    kv_all = last_key_at_or_before(p.mask, p.P, p.blk, kb, token_pos(p.mask, p.P, p.blk, qb, q_first)) + 1;
+    const int my_row = min(q_first + wave * 32 * G + lr, p.q_rows - 1);
+    lim = min(lim, last_key_at_or_before(p.mask, p.P, p.blk, kb, token_pos(p.mask, p.P, p.blk, qb, my_row)));
+    // Nothing visible and nothing to initialise or write: the state stays as it is.
+    if (kv_vis == 0 && p.flags == (kLoadState | kStoreState)) return;
+  }
+
   int64_t srow[G], st_row[G];
   bool row_ok[G];
 #pragma unroll
@@ -193,12 +214,13 @@ void fold_bf16_kernel(const FoldParams p) {
   // of the scaled score); it trails the true running maximum mtrue by less
   // than kLazy, which keeps every weight below 2^kLazy.  o and l are rescaled
   // to mtrue once, before they are stored.
-  float mref[G], mtrue[G], lpart[G];
+  float mref[G], mtrue[G], lpart[G], m_in[G];
   f32x16 oacc[G][NDB];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     if (p.flags & kLoadState) {
-      mref[g] = p.m[st_row[g]] * kLog2e;
+      m_in[g] = p.m[st_row[g]];
+      mref[g] = m_in[g] * kLog2e;
       lpart[g] = lg == 0 ? p.l[st_row[g]] : 0.0f;
       const float* orow = p.o + st_row[g] * D + 4 * lg;
 #pragma unroll
@@ -210,6 +232,7 @@ void fold_bf16_kernel(const FoldParams p) {
           for (int e = 0; e < 4; ++e) oacc[g][db][4 * j + e] = t[e];
         }
     } else {
+      m_in[g] = -INFINITY;
       mref[g] = -INFINITY;
       lpart[g] = 0.0f;
 #pragma unroll
@@ -222,8 +245,9 @@ void fold_bf16_kernel(const FoldParams p) {
 
   const __bf16* kbase = (const __bf16*)p.k + bi * p.k_sb + hi * p.k_sh + p.k_off[r];
   const __bf16* vbase = (const __bf16*)p.v + bi * p.v_sb + hi * p.v_sh + p.v_off[r];
-  const int n_full = p.kv_rows / TK;
-  const int n_kt = (p.kv_rows + TK - 1) / TK;
+  // Tiles [0, n_plain) need no mask; tiles [n_plain, n_kt) compare keys with lim.
+  const int n_plain = min(kv_all, p.kv_rows) / TK;
+  const int n_kt = (kv_vis + TK - 1) / TK;
   const float c2 = p.scale_log2;
 
   // Direct loads: chunk c of a tile is LDS units [64c, 64c + 64); lane i
@@ -293,12 +317,15 @@ void fold_bf16_kernel(const FoldParams p) {
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[g][c], s[kb], 0, 0, 0);
       }
   };
+  // Keys past this row's last visible key (the block's end, or the causal
+  // boundary) score -inf.
   auto mask = [&](f32x16 (&s)[NKB], int key0) {
+    const int lim_t = lim - key0 - 4 * lg;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        if (key0 + 32 * kb + 8 * (i >> 2) + 4 * lg + (i & 3) >= p.kv_rows) s[kb][i] = -INFINITY;
+        if (32 * kb + 8 * (i >> 2) + (i & 3) > lim_t) s[kb][i] = -INFINITY;
   };
   // Row maximum of the tile; raises mtrue, and mref when it falls more than
   // kLazy below the new maximum (rare: then o and l are rescaled here).  A
@@ -325,9 +352,11 @@ void fold_bf16_kernel(const FoldParams p) {
         for (int i = 0; i < 16; ++i) oacc[g][db][i] *= alpha;
     }
   };
-  // bf16 weights exp2(s c - mref) as packed pairs, and their sum into l.
+  // bf16 weights exp2(s c - mref) as packed pairs, and their sum into l.  A
+  // row that has seen no visible key yet (mref = -inf, every score -inf) gets
+  // weights exp2(-inf) = 0.
   auto weights = [&](const f32x16 (&s)[NKB], unsigned (&pk)[NKB][8], int g) {
-    const float mr = mref[g];
+    const float mr = mref[g] == -INFINITY ? 0.0f : mref[g];
     float lsum = 0.0f;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
@@ -360,8 +389,8 @@ void fold_bf16_kernel(const FoldParams p) {
       }
   };
 
-  // One tile whose K/V sit in LDS buffer `buf`; `ragged` masks keys past the end.
-  auto tile = [&](int kt, int buf, bool ragged) {
+  // One tile whose K/V sit in LDS buffer `buf`; `masked` applies lim.
+  auto tile = [&](int kt, int buf, bool masked) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile kt landed for this wave
     __syncthreads();                     // ... for every wave; the other buffer is free
     if (kt + 1 < n_kt) issue_tile(kt + 1, buf ^ 1);
@@ -370,7 +399,7 @@ void fold_bf16_kernel(const FoldParams p) {
     f32x16 sa[NKB];
     unsigned pa[NKB][8];
     scores(sa, kc, 0);
-    if (ragged) mask(sa, kt * TK);
+    if (masked) mask(sa, kt * TK);
     track_max(sa, 0);
     weights(sa, pa, 0);
     values(pa, vc, 0);
@@ -379,15 +408,15 @@ void fold_bf16_kernel(const FoldParams p) {
   if (n_kt > 0) {
     issue_tile(0, 0);
     int kt = 0;
-    for (; kt + 2 <= n_full; kt += 2) {
+    for (; kt + 2 <= n_plain; kt += 2) {
       tile(kt, 0, false);
       tile(kt + 1, 1, false);
     }
-    if (kt < n_full) {
+    if (kt < n_plain) {
       tile(kt, 0, false);
       ++kt;
     }
-    if (kt < n_kt) tile(kt, kt & 1, true);
+    for (; kt < n_kt; ++kt) tile(kt, kt & 1, true);
   }
 
 #pragma unroll
@@ -411,7 +440,8 @@ void fold_bf16_kernel(const FoldParams p) {
     }
     if (p.flags & kStoreState) {
       if (lg == 0) {
-        p.m[st_row[g]] = mtrue[g] * kLn2;
+        // A maximum that did not rise is stored exactly as it was loaded.
+        p.m[st_row[g]] = mtrue[g] == m_in[g] * kLog2e ? m_in[g] : mtrue[g] * kLn2;
         p.l[st_row[g]] = l_tot;
       }
       float* orow = p.o + st_row[g] * D + 4 * lg;

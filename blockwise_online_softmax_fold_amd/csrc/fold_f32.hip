@@ -10,6 +10,11 @@
 // and o columns in registers; partial dot products are combined across those
 // lanes with xor shuffles.  K and V stream through LDS in 32-key tiles, which
 // every row of the workgroup reads as broadcasts.
+//
+// Causal masking (math page, "Causal masking, load balance, and other
+// wrinkles"): the keys a row sees form a prefix of the visiting block in every
+// token layout, so the tile loop stops after the last key any row of the
+// workgroup sees and each row masks keys past its own last visible key.
 #include <math.h>
 
 #include "kernels.h"
@@ -44,6 +49,20 @@ __global__ __launch_bounds__(256) void fold_f32_kernel(const FoldParams p) {
   const int sub = tid % TPR;
   const int row = qt * ROWS + tid / TPR;
   const bool row_ok = row < p.q_rows;
+
+  // Keys [0, kv_vis) are visible to some row of this workgroup; key c is
+  // visible to this thread's row iff c <= lim.
+  int kv_vis = p.kv_rows;
+  int lim = p.kv_rows - 1;
+  if (p.mask != kMaskNone) {
+    const int qb = p.q_blk[r], kb = p.kv_blk[r];
+    const int q_last = min(qt * ROWS + ROWS, p.q_rows) - 1;
+    kv_vis = last_key_at_or_before(p.mask, p.P, p.blk, kb, token_pos(p.mask, p.P, p.blk, qb, q_last)) + 1;
+    const int my_row = min(row, p.q_rows - 1);
+    lim = min(lim, last_key_at_or_before(p.mask, p.P, p.blk, kb, token_pos(p.mask, p.P, p.blk, qb, my_row)));
+    // Nothing visible and nothing to initialise or write: the state stays as it is.
+    if (kv_vis == 0 && p.flags == (kLoadState | kStoreState)) return;
+  }
   const int64_t srow = (int64_t)r * p.q_rows + (row_ok ? row : p.q_rows - 1);
   const int col0 = 64 * sub;
 
@@ -59,10 +78,11 @@ __global__ __launch_bounds__(256) void fold_f32_kernel(const FoldParams p) {
   }
 
   const int64_t st_row = ((int64_t)bi * p.H + hi) * p.st_bh + srow;
-  float mc, l;
+  float mc, l, m_in;
   float ov[64];
   if (p.flags & kLoadState) {
-    mc = p.m[st_row] * kLog2e;
+    m_in = p.m[st_row];
+    mc = m_in * kLog2e;
     l = p.l[st_row];
     const float* op = p.o + st_row * D + col0;
 #pragma unroll
@@ -72,6 +92,7 @@ __global__ __launch_bounds__(256) void fold_f32_kernel(const FoldParams p) {
       for (int e = 0; e < 4; ++e) ov[4 * c + e] = t[e];
     }
   } else {
+    m_in = -INFINITY;
     mc = -INFINITY;
     l = 0.0f;
 #pragma unroll
@@ -80,7 +101,7 @@ __global__ __launch_bounds__(256) void fold_f32_kernel(const FoldParams p) {
 
   const float* kbase = (const float*)p.k + bi * p.k_sb + hi * p.k_sh + p.k_off[r];
   const float* vbase = (const float*)p.v + bi * p.v_sb + hi * p.v_sh + p.v_off[r];
-  const int n_kt = (p.kv_rows + kTileK - 1) / kTileK;
+  const int n_kt = (kv_vis + kTileK - 1) / kTileK;
   const float c2 = p.scale_log2;
 
   for (int kt = 0; kt < n_kt; ++kt) {
@@ -104,18 +125,21 @@ __global__ __launch_bounds__(256) void fold_f32_kernel(const FoldParams p) {
       for (int c = 0; c < 64; ++c) acc = fmaf(qv[c], kr[c], acc);
 #pragma unroll
       for (int x = 1; x < TPR; x <<= 1) acc += __shfl_xor(acc, x);
-      s[j] = key0 + j < p.kv_rows ? acc : -INFINITY;
+      s[j] = key0 + j <= lim ? acc : -INFINITY;
     }
     float mx = s[0];
 #pragma unroll
     for (int j = 1; j < kTileK; ++j) mx = fmaxf(mx, s[j]);
     const float m_new = fmaxf(mc, mx * c2);
-    const float alpha = __builtin_amdgcn_exp2f(mc - m_new);
+    // A row that has seen no visible key yet keeps (-inf, 0, 0): exponents are
+    // taken against 0 instead of -inf, so every weight is exp2(-inf) = 0.
+    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(mc - m_use);
     mc = m_new;
     float lsum = 0.0f;
 #pragma unroll
     for (int j = 0; j < kTileK; ++j) {
-      s[j] = __builtin_amdgcn_exp2f(fmaf(s[j], c2, -m_new));
+      s[j] = __builtin_amdgcn_exp2f(fmaf(s[j], c2, -m_use));
       lsum += s[j];
     }
     l = fmaf(l, alpha, lsum);
@@ -143,7 +167,8 @@ __global__ __launch_bounds__(256) void fold_f32_kernel(const FoldParams p) {
   }
   if (p.flags & kStoreState) {
     if (sub == 0) {
-      p.m[st_row] = mc * kLn2;
+      // A maximum that did not rise is stored exactly as it was loaded.
+      p.m[st_row] = mc == m_in * kLog2e ? m_in : mc * kLn2;
       p.l[st_row] = l;
     }
     float* op = p.o + st_row * D + col0;

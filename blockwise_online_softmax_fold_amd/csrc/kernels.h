@@ -41,7 +41,55 @@ struct FoldParams {
   int32_t q_rows, kv_rows;
   int32_t flags;
   float scale_log2;  // softmax scale times log2(e): scores are exponentiated in base 2
+  // Causal masking (mask != kMaskNone): query row r of resident r_ and key row c
+  // of its visiting block sit at sequence positions pos(q_blk[r_], r) and
+  // pos(kv_blk[r_], c) of a P-device ring with blocks of `blk` rows; keys after
+  // the query are masked.
+  int32_t mask;
+  int32_t P, blk;
+  int32_t q_blk[kMaxResident];
+  int32_t kv_blk[kMaxResident];
 };
+
+// Masking modes (the token layout of the ring when causal).
+enum MaskMode : int {
+  kMaskNone = 0,
+  kMaskContiguous = 1,  // device j holds tokens [j b, (j + 1) b)
+  kMaskStriped = 2,     // device j holds tokens j, j + P, j + 2P, ...
+  kMaskZigzag = 3,      // device j holds chunks j and 2P - 1 - j of b / 2 tokens
+};
+
+// Sequence position of row r of device j's block (blocks of b rows, P devices).
+__host__ __device__ inline int32_t token_pos(int mode, int32_t P, int32_t b, int32_t j, int32_t r) {
+  if (mode == kMaskStriped) return r * P + j;
+  if (mode == kMaskZigzag) {
+    const int32_t h = b >> 1;
+    return r < h ? j * h + r : (2 * P - 1 - j) * h + (r - h);
+  }
+  return j * b + r;
+}
+
+// Every layout numbers the rows of a block in increasing position (zig-zag:
+// chunk j < P comes before its mirror 2P - 1 - j), so the keys of device j's
+// block at or before a position x are a prefix of the block.  Largest such key
+// row (-1 if none).
+__host__ __device__ inline int32_t last_key_at_or_before(int mode, int32_t P, int32_t b, int32_t j, int32_t x) {
+  int32_t c;
+  if (mode == kMaskStriped) {
+    c = x < j ? -1 : (x - j) / P;
+  } else if (mode == kMaskZigzag) {
+    const int32_t h = b >> 1;
+    const int32_t hi0 = (2 * P - 1 - j) * h;  // position of the mirror chunk's first row
+    if (x >= hi0)
+      c = h + (x - hi0);
+    else
+      c = x - j * h < h ? x - j * h : h - 1;
+  } else {
+    c = x - j * b;
+  }
+  if (c < -1) c = -1;
+  return c < b - 1 ? c : b - 1;
+}
 
 // Each launcher returns the launch status (hipGetLastError after the launch).
 hipError_t launch_fold_bf16(const FoldParams& p, int d, hipStream_t s);

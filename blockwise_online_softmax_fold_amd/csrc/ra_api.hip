@@ -271,7 +271,7 @@ bool env_flag(const char* name) {
 
 RA_API const char* ra_last_error(void) { return g_err.c_str(); }
 
-RA_API const char* ra_version(void) { return "0.1.0"; }
+RA_API const char* ra_version(void) { return "0.2.0"; }
 
 RA_API ra_status_t ra_state_init(float* m, float* l, float* o, int64_t B, int64_t H, int64_t rows, int64_t d,
                                  void* stream) {
@@ -285,11 +285,13 @@ RA_API ra_status_t ra_state_init(float* m, float* l, float* o, int64_t B, int64_
   return RA_OK;
 }
 
-RA_API ra_status_t ra_fold_block(const void* q, const int64_t q_strides[3], const void* k, const int64_t k_strides[3],
-                                 const void* v, const int64_t v_strides[3], ra_dtype_t dt, int64_t B, int64_t H,
-                                 int64_t q_rows, int64_t kv_rows, int64_t d, float scale, float* m, float* l,
-                                 float* o, void* stream) {
-  g_err.clear();
+namespace {
+
+// Shared body of ra_fold_block and ra_fold_block_causal.
+ra_status_t fold_block_impl(const void* q, const int64_t q_strides[3], const void* k, const int64_t k_strides[3],
+                            const void* v, const int64_t v_strides[3], ra_dtype_t dt, int64_t B, int64_t H,
+                            int64_t q_rows, int64_t kv_rows, int64_t d, float scale, float* m, float* l, float* o,
+                            int mask, int32_t P, int32_t q_block, int32_t kv_block, void* stream) {
   ra_status_t st = check_common(dt, B, H, d);
   if (st != RA_OK) return st;
   if (q_rows < 0 || kv_rows < 0) return fail(RA_E_INVALID_ARG, "q_rows and kv_rows must be >= 0");
@@ -327,8 +329,59 @@ RA_API ra_status_t ra_fold_block(const void* q, const int64_t q_strides[3], cons
   p.kv_rows = (int32_t)kv_rows;
   p.flags = ra::kLoadState | ra::kStoreState;
   p.scale_log2 = to_log2_scale(sc);
+  p.mask = mask;
+  p.P = P;
+  p.blk = (int32_t)kv_rows;
+  p.q_blk[0] = q_block;
+  p.kv_blk[0] = kv_block;
   RA_HIP(launch_fold(p, dt, (int)d, (hipStream_t)stream), "fold launch");
   return RA_OK;
+}
+
+bool valid_layout(int layout) {
+  return layout == RA_CAUSAL_NONE || layout == RA_CAUSAL_CONTIGUOUS || layout == RA_CAUSAL_STRIPED ||
+         layout == RA_CAUSAL_ZIGZAG;
+}
+
+// Positions of a causal ring (P blocks of b rows) must fit the kernels' int32.
+ra_status_t check_causal(int layout, int64_t P, int64_t b) {
+  if (!valid_layout(layout)) return fail(RA_E_INVALID_ARG, "unknown causal layout %d", layout);
+  if (layout == RA_CAUSAL_NONE) return RA_OK;
+  if (P * b > 0x7fffffffLL) return fail(RA_E_UNSUPPORTED, "P*b=%lld positions do not fit 32 bits", (long long)(P * b));
+  if (layout == RA_CAUSAL_ZIGZAG && b % 2 != 0)
+    return fail(RA_E_INVALID_ARG, "zig-zag layout needs an even block size, got %lld", (long long)b);
+  return RA_OK;
+}
+
+}  // namespace
+
+RA_API ra_status_t ra_fold_block(const void* q, const int64_t q_strides[3], const void* k, const int64_t k_strides[3],
+                                 const void* v, const int64_t v_strides[3], ra_dtype_t dt, int64_t B, int64_t H,
+                                 int64_t q_rows, int64_t kv_rows, int64_t d, float scale, float* m, float* l,
+                                 float* o, void* stream) {
+  g_err.clear();
+  return fold_block_impl(q, q_strides, k, k_strides, v, v_strides, dt, B, H, q_rows, kv_rows, d, scale, m, l, o,
+                         ra::kMaskNone, 1, 0, 0, stream);
+}
+
+RA_API ra_status_t ra_fold_block_causal(const void* q, const int64_t q_strides[3], const void* k,
+                                        const int64_t k_strides[3], const void* v, const int64_t v_strides[3],
+                                        ra_dtype_t dt, int64_t B, int64_t H, int64_t rows, int64_t d, float scale,
+                                        ra_causal_t layout, int32_t P, int32_t q_block, int32_t kv_block, float* m,
+                                        float* l, float* o, void* stream) {
+  g_err.clear();
+  ra_status_t st;
+  if (!valid_layout((int)layout)) return fail(RA_E_INVALID_ARG, "unknown causal layout %d", (int)layout);
+  if (layout != RA_CAUSAL_NONE) {
+    if (P < 1) return fail(RA_E_INVALID_ARG, "P=%d must be >= 1", (int)P);
+    if (q_block < 0 || q_block >= P || kv_block < 0 || kv_block >= P)
+      return fail(RA_E_INVALID_ARG, "q_block=%d and kv_block=%d must lie in [0, P=%d)", (int)q_block, (int)kv_block,
+                  (int)P);
+    if (rows < 0) return fail(RA_E_INVALID_ARG, "rows=%lld must be >= 0", (long long)rows);
+    if ((st = check_causal((int)layout, P, rows)) != RA_OK) return st;
+  }
+  return fold_block_impl(q, q_strides, k, k_strides, v, v_strides, dt, B, H, rows, rows, d, scale, m, l, o,
+                         (int)layout, P, q_block, kv_block, stream);
 }
 
 RA_API ra_status_t ra_finalize(const float* l, const float* o, void* out, const int64_t out_strides[3],
@@ -357,15 +410,17 @@ RA_API size_t ra_ring_workspace_bytes(ra_dtype_t dt, int64_t B, int64_t H, int64
   return ring_layout(dt, B, H, N, d, P, n_q).total;
 }
 
-RA_API ra_status_t ra_ring_forward(const void* q, const int64_t q_strides[3], const void* k,
-                                   const int64_t k_strides[3], const void* v, const int64_t v_strides[3], void* out,
-                                   const int64_t out_strides[3], ra_dtype_t dt, int64_t B, int64_t H, int64_t N,
-                                   int64_t d, int32_t P, const int32_t* query_blocks, int32_t n_q, float scale,
-                                   void* workspace, size_t workspace_bytes, void* stream_) {
-  g_err.clear();
+namespace {
+
+ra_status_t ring_forward_impl(const void* q, const int64_t q_strides[3], const void* k, const int64_t k_strides[3],
+                              const void* v, const int64_t v_strides[3], void* out, const int64_t out_strides[3],
+                              ra_dtype_t dt, int64_t B, int64_t H, int64_t N, int64_t d, int32_t P,
+                              const int32_t* query_blocks, int32_t n_q, float scale, int mask, void* workspace,
+                              size_t workspace_bytes, void* stream_) {
   ra_status_t st = check_ring(q, q_strides, k, k_strides, v, v_strides, out, out_strides, dt, B, H, N, d, P,
                               query_blocks, n_q);
   if (st != RA_OK) return st;
+  if ((st = check_causal(mask, P, N / P)) != RA_OK) return st;
   float sc;
   if ((st = resolve_scale(scale, d, &sc)) != RA_OK) return st;
   const RingLayout L = ring_layout(dt, B, H, N, d, P, n_q);
@@ -458,6 +513,14 @@ RA_API ra_status_t ra_ring_forward(const void* q, const int64_t q_strides[3], co
       p.kv_rows = (int32_t)b;
       p.flags = (t == 0 ? 0 : ra::kLoadState) | (t == P - 1 ? ra::kWriteOut : ra::kStoreState);
       p.scale_log2 = to_log2_scale(sc);
+      p.mask = mask;
+      p.P = P;
+      p.blk = (int32_t)b;
+      for (int32_t r = 0; r < nr; ++r) {
+        const int32_t i = qb(r0 + r);
+        p.q_blk[r] = i;
+        p.kv_blk[r] = (int32_t)(((int64_t)i - t) % P + P) % P;
+      }
       const long pi = prof_begin(stream);
       RA_HIP(launch_fold(p, dt, (int)d, stream), "fold launch");
       prof_end(pi, stream);
@@ -471,6 +534,30 @@ RA_API ra_status_t ra_ring_forward(const void* q, const int64_t q_strides[3], co
   }
   if (own_ws) RA_HIP(hipFreeAsync(ws, stream), "hipFreeAsync (ring workspace)");
   return RA_OK;
+}
+
+}  // namespace
+
+RA_API ra_status_t ra_ring_forward(const void* q, const int64_t q_strides[3], const void* k,
+                                   const int64_t k_strides[3], const void* v, const int64_t v_strides[3], void* out,
+                                   const int64_t out_strides[3], ra_dtype_t dt, int64_t B, int64_t H, int64_t N,
+                                   int64_t d, int32_t P, const int32_t* query_blocks, int32_t n_q, float scale,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  return ring_forward_impl(q, q_strides, k, k_strides, v, v_strides, out, out_strides, dt, B, H, N, d, P,
+                           query_blocks, n_q, scale, ra::kMaskNone, workspace, workspace_bytes, stream);
+}
+
+RA_API ra_status_t ra_ring_forward_causal(const void* q, const int64_t q_strides[3], const void* k,
+                                          const int64_t k_strides[3], const void* v, const int64_t v_strides[3],
+                                          void* out, const int64_t out_strides[3], ra_dtype_t dt, int64_t B,
+                                          int64_t H, int64_t N, int64_t d, int32_t P, const int32_t* query_blocks,
+                                          int32_t n_q, float scale, ra_causal_t layout, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  if (!valid_layout((int)layout)) return fail(RA_E_INVALID_ARG, "unknown causal layout %d", (int)layout);
+  return ring_forward_impl(q, q_strides, k, k_strides, v, v_strides, out, out_strides, dt, B, H, N, d, P,
+                           query_blocks, n_q, scale, (int)layout, workspace, workspace_bytes, stream);
 }
 
 RA_API ra_status_t ra_profile_folds(int enable) {

@@ -60,6 +60,31 @@ typedef enum {
 typedef enum { RA_DTYPE_F32 = 0, RA_DTYPE_BF16 = 1 } ra_dtype_t;
 
 /*
+ * Causal masking and the token layout it assumes.  A query sees only keys at
+ * or before its own position (math page, "Causal masking, load balance, and
+ * other wrinkles"; bembew.net "Implementation Considerations", causal
+ * masking).  The ring's N = P*b tokens are dealt to the P devices in one of
+ * three ways (vibeengines.com, "The causal-mask catch"); row r (0 <= r < b) of
+ * device j's block holds sequence position
+ *   RA_CAUSAL_CONTIGUOUS: j*b + r                     (contiguous split)
+ *   RA_CAUSAL_STRIPED:    r*P + j                     (round-robin, "striped")
+ *   RA_CAUSAL_ZIGZAG:     j*h + r          for r < h  (h = b/2: chunk j and its
+ *                         (2P-1-j)*h + r-h for r >= h  mirror chunk 2P-1-j)
+ * RA_CAUSAL_NONE is full (non-causal) attention.  In every layout positions
+ * rise with r, so the keys a query row sees form a prefix of each block; the
+ * kernels skip whole key tiles past the last visible key (a block entirely in
+ * a row's future costs no arithmetic) and mask keys only inside the tiles
+ * that straddle the boundary.  A row that sees no key of a block keeps its
+ * state exactly as it was (m' = -inf is guarded: alpha = 1, weights 0).
+ */
+typedef enum {
+  RA_CAUSAL_NONE = 0,
+  RA_CAUSAL_CONTIGUOUS = 1,
+  RA_CAUSAL_STRIPED = 2,
+  RA_CAUSAL_ZIGZAG = 3
+} ra_causal_t;
+
+/*
  * ra_state_init -- set (m, l, o) = (-inf, 0, 0) for B*H*rows query rows.
  * Math page, "Accumulation math, step by step" (loop set-up).
  * m, l: [B, H, rows] float32; o: [B, H, rows, d] float32; all contiguous.
@@ -87,6 +112,23 @@ ra_status_t ra_fold_block(const void* q, const int64_t q_strides[3], const void*
                           const void* v, const int64_t v_strides[3], ra_dtype_t dt, int64_t B, int64_t H,
                           int64_t q_rows, int64_t kv_rows, int64_t d, float scale, float* m, float* l, float* o,
                           void* stream);
+
+/*
+ * ra_fold_block_causal -- ra_fold_block under a causal mask: the query block
+ * is device q_block's and the visiting block device kv_block's of a P-device
+ * ring in the given layout, both of b = rows rows (so q and k, v have the
+ * same row count), 0 <= q_block, kv_block < P.  Arguments and state as for
+ * ra_fold_block.  RA_CAUSAL_ZIGZAG needs rows even; P*rows must stay below
+ * 2^31.  layout RA_CAUSAL_NONE is exactly ra_fold_block with q_rows = kv_rows
+ * = rows (P, q_block, kv_block are then ignored).  A pair with no visible key
+ * (for instance kv_block > q_block in the contiguous layout) leaves the state
+ * bit for bit as it was.
+ */
+ra_status_t ra_fold_block_causal(const void* q, const int64_t q_strides[3], const void* k,
+                                 const int64_t k_strides[3], const void* v, const int64_t v_strides[3],
+                                 ra_dtype_t dt, int64_t B, int64_t H, int64_t rows, int64_t d, float scale,
+                                 ra_causal_t layout, int32_t P, int32_t q_block, int32_t kv_block, float* m,
+                                 float* l, float* o, void* stream);
 
 /*
  * ra_finalize -- O = o / l after the last block (math page, end of the loop).
@@ -135,6 +177,22 @@ ra_status_t ra_ring_forward(const void* q, const int64_t q_strides[3], const voi
                             ra_dtype_t dt, int64_t B, int64_t H, int64_t N, int64_t d, int32_t P,
                             const int32_t* query_blocks, int32_t n_q, float scale, void* workspace,
                             size_t workspace_bytes, void* stream);
+
+/*
+ * ra_ring_forward_causal -- ra_ring_forward under a causal mask.  q, k, v and
+ * out are in the layout's device order: block j (rows [j*b, (j+1)*b)) is
+ * device j's share, holding the positions given above for `layout`.  Every
+ * other argument, the workspace and the schedule are those of
+ * ra_ring_forward; RA_CAUSAL_ZIGZAG needs b even and N must stay below 2^31.
+ * Steps whose visiting block lies entirely in the resident block's future
+ * fold nothing (the hand-off still moves the block, as the ring would).
+ * Every row sees at least its own position, so no output row has l = 0.
+ */
+ra_status_t ra_ring_forward_causal(const void* q, const int64_t q_strides[3], const void* k,
+                                   const int64_t k_strides[3], const void* v, const int64_t v_strides[3], void* out,
+                                   const int64_t out_strides[3], ra_dtype_t dt, int64_t B, int64_t H, int64_t N,
+                                   int64_t d, int32_t P, const int32_t* query_blocks, int32_t n_q, float scale,
+                                   ra_causal_t layout, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Measurement support (not part of the method).  While enabled on the calling

@@ -139,3 +139,51 @@ def test_state_init_and_finalize_reject(lib):
     assert lib.ra_state_init(A, A, A, 1, 1, 0, 64, None) == 0
     assert lib.ra_finalize(A, A, ctypes.c_void_p(None), S_BF16, BF16, 1, 1, 4, 64, None) == 1
     assert lib.ra_finalize(A, A, A, S_BF16, 9, 1, 1, 4, 64, None) == 1
+
+
+def _fold_causal(lib, layout=1, P=4, qb=0, kb=0, rows=1024, dt=BF16, d=128, q=A, k=A, m=A):
+    return lib.ra_fold_block_causal(q, S_BF16, k, S_BF16, A, S_BF16, dt, 1, 16, rows, d, ctypes.c_float(0.0),
+                                    layout, P, qb, kb, m, A, A, None)
+
+
+@pytest.mark.parametrize("kwargs,status,needle", [
+    (dict(layout=9), 1, "unknown causal layout"),
+    (dict(layout=-1), 1, "unknown causal layout"),
+    (dict(P=0), 1, "P=0"),
+    (dict(qb=4), 1, "must lie in [0, P=4)"),
+    (dict(kb=-1), 1, "must lie in [0, P=4)"),
+    (dict(layout=3, rows=1023), 1, "even block size"),
+    (dict(layout=2, P=1 << 22, rows=1024), 2, "do not fit 32 bits"),
+    (dict(rows=-5), 1, "rows=-5"),
+    (dict(q=ctypes.c_void_p(None)), 1, "q is NULL"),
+    (dict(m=ctypes.c_void_p(None)), 1, "NULL"),
+    (dict(d=80), 2, "head dim"),
+])
+def test_fold_block_causal_rejects(lib, kwargs, status, needle):
+    assert _fold_causal(lib, **kwargs) == status
+    assert needle in lib.ra_last_error().decode()
+
+
+def test_fold_block_causal_empty_and_none_layout_without_gpu(lib):
+    N = ctypes.c_void_p(None)
+    assert _fold_causal(lib, rows=0, q=N, k=N, m=N) == 0
+    assert _fold_causal(lib, layout=3, rows=0, q=N, k=N, m=N) == 0
+    # RA_CAUSAL_NONE ignores P and the block ids, like ra_fold_block
+    assert _fold_causal(lib, layout=0, P=0, qb=7, kb=-3, rows=0) == 0
+    assert lib.ra_last_error().decode() == ""
+
+
+def _ring_causal(lib, layout=1, N=131072, P=16, n_q=16, d=128):
+    return lib.ra_ring_forward_causal(A, S_BF16, A, S_BF16, A, S_BF16, A, S_BF16, BF16, 1, 32, N, d, P, None, n_q,
+                                      ctypes.c_float(0.0), layout, ctypes.c_void_p(None), 0, None)
+
+
+@pytest.mark.parametrize("kwargs,status,needle", [
+    (dict(layout=4), 1, "unknown causal layout"),
+    (dict(layout=3, N=16 * 1001), 1, "even block size"),
+    (dict(layout=1, N=1000), 2, "not a multiple"),
+    (dict(layout=2, d=48), 2, "head dim"),
+])
+def test_ring_forward_causal_rejects(lib, kwargs, status, needle):
+    assert _ring_causal(lib, **kwargs) == status
+    assert needle in lib.ra_last_error().decode()
