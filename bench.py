@@ -7,10 +7,13 @@ query block, including the final normalisation.  Inputs are resident in HBM
 before timing starts.  Prints ONE JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
+                    [--causal contiguous|striped|zigzag]
                     [--no-cpu-baseline] [--cpu-seconds S]
 
 The default workload is the 128K-token ring (B1 H32 d128 N131072 P16, all 16
-query blocks resident).
+query blocks resident), non-causal.  With --causal the same inputs are taken
+as dealt to the devices in that token layout and the causal ring runs; its
+TFLOP/s count only the visible (query, key) pairs, 4 d FLOP each.
 """
 
 from __future__ import annotations
@@ -50,6 +53,27 @@ def _traffic(workload: str, dtype: str):
     if not ent or ent.get("source_sha256_16") != _source_hash(dtype):
         return None
     return ent.get("hbm_bytes_per_launch")
+
+
+def _positions(layout: str, P: int, b: int):
+    """Sequence position of row r of device j's block for a causal layout."""
+    import numpy as np
+
+    j = np.arange(P)[:, None]
+    r = np.arange(b)[None, :]
+    if layout == "contiguous":
+        return j * b + r
+    if layout == "striped":
+        return r * P + j
+    h = b // 2
+    return np.where(r < h, j * h + r, (2 * P - 1 - j) * h + (r - h))
+
+
+def _visible_pairs(w, layout: str) -> float:
+    """(query, key) pairs a causal ring attends to: a row at position x sees
+    the x + 1 positions 0..x, per batch and head."""
+    pos = _positions(layout, w.P, w.b)
+    return float(w.B) * w.H * float(sum(int(pos[i].sum()) + w.b for i in w.resident))
 
 
 def _blas_threads() -> int:
@@ -104,6 +128,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--causal", choices=("contiguous", "striped", "zigzag"), default=None,
+                    help="run the causal ring with the inputs in this token layout")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -135,7 +161,10 @@ def main() -> int:
     qb = w.query_blocks
 
     def step():
-        ra.ra_ring_forward(q, k, v, w.P, query_blocks=qb, out=out, workspace=ws)
+        if args.causal:
+            ra.ra_ring_forward_causal(q, k, v, w.P, args.causal, query_blocks=qb, out=out, workspace=ws)
+        else:
+            ra.ra_ring_forward(q, k, v, w.P, query_blocks=qb, out=out, workspace=ws)
 
     if args.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
@@ -163,7 +192,7 @@ def main() -> int:
     ra.ra_profile_folds(False)
     print(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
 
-    flops = w.flops()
+    flops = w.flops() if not args.causal else 4.0 * w.d * _visible_pairs(w, args.causal)
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK[w.dtype]
     launches_per_step = launches / args.steps
@@ -197,9 +226,9 @@ def main() -> int:
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "P": w.P, "b": w.b,
-                   "resident_query_blocks": w.n_q, "seed": w.seed, "causal": False},
+                   "resident_query_blocks": w.n_q, "seed": w.seed, "causal": args.causal or False},
         "pct_mfma_peak": round(100.0 * tflops / peak, 2),
-        "exps_per_s": w.exps() / (ms * 1e-3),
+        "exps_per_s": (w.exps() if not args.causal else _visible_pairs(w, args.causal)) / (ms * 1e-3),
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
