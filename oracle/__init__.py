@@ -18,11 +18,15 @@ Everything here is plain NumPy in float64, written from the pages:
   (i - t) mod P, finished with o / l (math page, "The ring schedule" and
   "Accumulation math, step by step").
 * ``ring_schedule`` -- the block a device holds at each step.
+* ``block_bounds`` -- the rows of each device's block; when N is not a
+  multiple of P the first N mod P blocks hold one row more (bembew.net
+  "Implementation Considerations", load balancing).
 * ``layouts`` -- contiguous, striped and zig-zag token layouts and the causal
   positions they imply (math page "Causal masking, load balance, and other
   wrinkles"; vibeengines.com "The causal-mask catch").
 
-Every function here is pinned by ``tests/test_oracle.py`` against values the
+Every function here is pinned (``tests/test_oracle.py``, ``test_oracle_causal.py``,
+``test_oracle_ragged.py``) against values the
 pages print (the worked two-block example), closed forms, a brute-force
 pure-Python evaluation, a library routine (torch's fp64 CPU attention) and
 invariants the pages state (order independence, P = 1).
@@ -32,6 +36,7 @@ from . import layouts
 from .attention import dense_attention, dense_attention_rows
 from .ring import (
     State,
+    block_bounds,
     finalize,
     fold,
     init_state,
@@ -41,6 +46,7 @@ from .ring import (
 
 __all__ = [
     "State",
+    "block_bounds",
     "layouts",
     "dense_attention",
     "dense_attention_rows",

@@ -14,6 +14,13 @@ Sources:
 ``positions(layout, P, b)`` returns pos[j, r], the position in the whole
 sequence of row r of device j's shard.  A tensor "in layout order" holds
 device j's shard as rows [j*b, (j+1)*b) of its sequence axis.
+
+When N is not a multiple of P (bembew.net "Ring Attention", "Implementation
+Considerations": padding or dynamic partitioning is needed), the shards are
+uneven: ``block_positions(layout, P, N)`` lists each device's positions.  The
+contiguous split gives the first N mod P devices one token more (the sizes
+``numpy.array_split`` makes); dealing tokens round-robin (striped) gives
+exactly the same sizes.  The zig-zag split needs N to be a multiple of 2P.
 """
 
 from __future__ import annotations
@@ -38,17 +45,39 @@ def positions(layout: str, P: int, b: int) -> np.ndarray:
     raise ValueError(f"unknown layout {layout!r}")
 
 
+def block_sizes(P: int, N: int) -> list[int]:
+    """Rows of each device's shard: N // P, plus one for the first N mod P."""
+    return [N // P + (1 if j < N % P else 0) for j in range(P)]
+
+
+def block_positions(layout: str, P: int, N: int) -> list[np.ndarray]:
+    """Positions held by each device, in row order, for any N >= P."""
+    if N % P == 0:
+        return list(positions(layout, P, N // P))
+    sizes = block_sizes(P, N)
+    if layout == "contiguous":
+        starts = np.concatenate([[0], np.cumsum(sizes)])
+        return [np.arange(starts[j], starts[j] + sizes[j]) for j in range(P)]
+    if layout == "striped":
+        return [j + P * np.arange(sizes[j]) for j in range(P)]
+    if layout == "zigzag":
+        raise ValueError("zig-zag needs N to be a multiple of 2P")
+    raise ValueError(f"unknown layout {layout!r}")
+
+
+def _perm(layout: str, P: int, n: int) -> np.ndarray:
+    return np.concatenate(block_positions(layout, P, n))
+
+
 def to_layout(x, layout: str, P: int):
     """Reorder the sequence axis (-2) of x from natural order to layout order."""
-    n = x.shape[-2]
-    perm = positions(layout, P, n // P).reshape(-1)
-    return x[..., perm, :]
+    return x[..., _perm(layout, P, x.shape[-2]), :]
 
 
 def from_layout(x, layout: str, P: int):
     """Inverse of ``to_layout``."""
     n = x.shape[-2]
-    perm = positions(layout, P, n // P).reshape(-1)
+    perm = _perm(layout, P, n)
     inv = np.empty_like(perm)
     inv[perm] = np.arange(n)
     return x[..., inv, :]

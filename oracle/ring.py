@@ -15,6 +15,9 @@ Sources:
     block, fold P times, finish with O_i = o / l.
 * bembew.net "Ring Attention", "Conceptual Algorithm": the same loop with
   m_new = max(m, rowmax S), alpha = exp(m - m_new), beta = exp(S - m_new).
+* bembew.net "Implementation Considerations", load balancing: when N is not a
+  multiple of P the shards cannot be equal; here the first N mod P devices
+  hold one row more (block j starts at j (N // P) + min(j, N mod P)).
 
 The steps below follow those passages in order, one block at a time, with no
 tiling inside a block and no reordering.
@@ -99,6 +102,14 @@ def finalize(state: State) -> np.ndarray:
     return np.where(l > 0, state.o / safe, 0.0)
 
 
+def block_bounds(N: int, P: int) -> list[tuple[int, int]]:
+    """[start, stop) rows of each device's block: N // P rows each, one more
+    for the first N mod P devices."""
+    b, rem = divmod(N, P)
+    starts = [j * b + min(j, rem) for j in range(P + 1)]
+    return [(starts[j], starts[j + 1]) for j in range(P)]
+
+
 def ring_schedule(P: int, i: int) -> list[int]:
     """Block held by device i on steps t = 0..P-1: (i - t) mod P (math page,
     "The ring schedule")."""
@@ -118,7 +129,8 @@ def ring_attention(
 ):
     """Run the per-device loop for each resident query block.
 
-    q, k, v: [..., N, d] with N = P * b (the whole sequence).
+    q, k, v: [..., N, d], the whole sequence, any N >= P (uneven blocks when
+      N is not a multiple of P, see ``block_bounds``).
     query_blocks: which devices' query blocks to compute (default 0..P-1).
     order: maps a device index i to the sequence of blocks it folds
       (default: the ring schedule (i - t) mod P).  The math page's worked
@@ -128,16 +140,16 @@ def ring_attention(
       "zigzag": then q, k, v are in that layout's device order (see
       ``oracle.layouts``) and a query sees only keys at or before its position.
     Returns O for the resident blocks stacked along the row axis
-    ([..., len(query_blocks) * b, dv]); with ``return_states`` also the list,
+    ([..., sum of their sizes, dv]); with ``return_states`` also the list,
     per resident block, of the state after every step.
     """
     q = _as_f64(q)
     k = _as_f64(k)
     v = _as_f64(v)
     n = k.shape[-2]
-    if n % P != 0:
-        raise ValueError(f"N={n} is not a multiple of P={P}")
-    b = n // P
+    if not 1 <= P <= n:
+        raise ValueError(f"need 1 <= P={P} <= N={n}")
+    bounds = block_bounds(n, P)
     if query_blocks is None:
         query_blocks = range(P)
     if order is None:
@@ -146,18 +158,20 @@ def ring_attention(
     dv = v.shape[-1]
     pos = None
     if causal_layout is not None:
-        from .layouts import positions
+        from .layouts import block_positions
 
-        pos = positions(causal_layout, P, b)
+        pos = block_positions(causal_layout, P, n)
     outs = []
     all_states = []
     for i in query_blocks:
-        q_i = q[..., i * b:(i + 1) * b, :]
-        state = init_state(lead, b, dv)
+        q_i = q[..., bounds[i][0]:bounds[i][1], :]
+        state = init_state(lead, q_i.shape[-2], dv)
         states = []
         for j in order(i):
             qp, kp = (None, None) if pos is None else (pos[i], pos[j])
-            state = fold(state, q_i, k[..., j * b:(j + 1) * b, :], v[..., j * b:(j + 1) * b, :], scale, qp, kp)
+            k_j = k[..., bounds[j][0]:bounds[j][1], :]
+            v_j = v[..., bounds[j][0]:bounds[j][1], :]
+            state = fold(state, q_i, k_j, v_j, scale, qp, kp)
             states.append(state.copy())
         outs.append(finalize(state))
         all_states.append(states)
