@@ -80,7 +80,7 @@ def load() -> ctypes.CDLL:
                                   vp, vp, vp, vp]
     lib.ra_fold_block.restype = ctypes.c_int
     lib.ra_fold_block_causal.argtypes = [vp, strides, vp, strides, vp, strides, ctypes.c_int, i64, i64, i64, i64,
-                                         f32, ctypes.c_int, i32, i32, i32, vp, vp, vp, vp]
+                                         f32, ctypes.c_int, i32, i32, i32, vp, vp, vp, vp]  # (..., B, H, N, d, ...)
     lib.ra_fold_block_causal.restype = ctypes.c_int
     lib.ra_finalize.argtypes = [vp, vp, vp, strides, ctypes.c_int, i64, i64, i64, i64, vp]
     lib.ra_finalize.restype = ctypes.c_int
@@ -198,23 +198,37 @@ def _layout_code(layout) -> int:
     return CAUSAL_LAYOUTS[layout]
 
 
-def ra_fold_block_causal(q, k, v, m, l, o, layout, P: int, q_block: int, kv_block: int, scale: float = 0.0,
-                         stream=None) -> None:
+def block_sizes(N: int, P: int) -> list:
+    """Rows of each device's block: N // P, one more for the first N % P."""
+    return [N // P + (1 if j < N % P else 0) for j in range(P)]
+
+
+def ra_fold_block_causal(q, k, v, m, l, o, layout, P: int, q_block: int, kv_block: int, N: int | None = None,
+                         scale: float = 0.0, stream=None) -> None:
     """Fold device kv_block's block into device q_block's state under the causal
-    mask of a P-device ring in ``layout`` ("contiguous", "striped", "zigzag");
-    q, k, v: [B, H, b, d]."""
+    mask of a P-device ring over N tokens in ``layout`` ("contiguous",
+    "striped", "zigzag"); q: [B, H, n_qblock, d], k, v: [B, H, n_kvblock, d].
+    N defaults to P * rows when q and k have the same row count."""
     _state_ok(m, l, o)
     B, H, rows, d = q.shape
-    if k.shape != v.shape or k.shape != q.shape:
-        raise ValueError(f"q, k and v must share one [B, H, b, d] shape: {tuple(q.shape)}, {tuple(k.shape)}, "
-                         f"{tuple(v.shape)}")
+    if N is None:
+        if k.shape[2] != rows:
+            raise ValueError("N is needed when the two blocks differ in size")
+        N = P * rows
+    if P >= 1 and N >= P and 0 <= q_block < P and 0 <= kv_block < P:
+        sizes = block_sizes(N, P)
+        if rows != sizes[q_block] or k.shape[2] != sizes[kv_block]:
+            raise ValueError(f"blocks {q_block} and {kv_block} of N={N} over P={P} have {sizes[q_block]} and "
+                             f"{sizes[kv_block]} rows; q has {rows}, k has {k.shape[2]}")
+    if k.shape != v.shape or k.shape[:2] != q.shape[:2] or k.shape[3] != d:
+        raise ValueError(f"shapes q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)} do not match")
     if tuple(o.shape) != (B, H, rows, d) or tuple(m.shape) != (B, H, rows) or tuple(l.shape) != (B, H, rows):
         raise ValueError("state shapes do not match q")
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k and v must have one dtype")
     _check(load().ra_fold_block_causal(
         _dev(q, "q"), _strides(q), _dev(k, "k"), _strides(k), _dev(v, "v"), _strides(v), _dtype_code(q),
-        B, H, rows, d, float(scale), _layout_code(layout), int(P), int(q_block), int(kv_block),
+        B, H, int(N), d, float(scale), _layout_code(layout), int(P), int(q_block), int(kv_block),
         _dev(m, "m"), _dev(l, "l"), _dev(o, "o"), _stream(stream)))
 
 
@@ -251,8 +265,13 @@ def _ring(q, k, v, P, query_blocks, out, scale, workspace, stream, layout):
     if v.shape != k.shape:
         raise ValueError("k and v must have the same shape")
     n_q = P if query_blocks is None else len(query_blocks)
-    if P >= 1 and N % P == 0 and (q.shape[:2] != k.shape[:2] or q.shape[3] != d or q.shape[2] != n_q * (N // P)):
-        raise ValueError(f"q must be [B, H, n_q*N/P, d] = [{B}, {H}, {n_q * (N // P)}, {d}], got {tuple(q.shape)}")
+    if 1 <= P <= N:
+        sizes = block_sizes(N, P)
+        qb = range(P) if query_blocks is None else query_blocks
+        rows = sum(sizes[i] for i in qb if 0 <= i < P)
+        if q.shape[:2] != k.shape[:2] or q.shape[3] != d or q.shape[2] != rows:
+            raise ValueError(f"q must be [B, H, rows of the resident blocks, d] = [{B}, {H}, {rows}, {d}], "
+                             f"got {tuple(q.shape)}")
     if out is not None and out.shape != q.shape:
         raise ValueError("out must have q's shape")
     if out is None:

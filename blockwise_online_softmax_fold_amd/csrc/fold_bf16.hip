@@ -177,17 +177,23 @@ void fold_bf16_kernel(const FoldParams p) {
   const int lr = lane & 31;
   const int lg = lane >> 5;
 
+  // This resident's block lengths; a query tile past its end has nothing to do.
+  const int q_len = p.q_len[r], kv_len = p.kv_len[r];
+  if (qt * QT >= q_len) return;
+
   // Keys [0, kv_vis) are visible to some row of this workgroup, keys
   // [0, kv_all) to every row; key c is visible to this lane's row iff c <= lim.
-  int kv_vis = p.kv_rows, kv_all = p.kv_rows;
-  int lim = p.kv_rows - 1;
+  int kv_vis = kv_len, kv_all = kv_len;
+  int lim = kv_len - 1;
   if (p.mask != kMaskNone) {
     const int qb = p.q_blk[r], kb = p.kv_blk[r];
-    const int q_first = qt * QT, q_last = min(q_first + QT, p.q_rows) - 1;
-    kv_vis = last_key_at_or_before(p.mask, p.P, p.blk, kb, token_pos(p.mask, p.P, p.blk, qb, q_last)) + 1;
-    kv_all = last_key_at_or_before(p.mask, p.P, p.blk, kb, token_pos(p.mask, p.P, p.blk, qb, q_first)) + 1;
-    const int my_row = min(q_first + wave * 32 * G + lr, p.q_rows - 1);
-    lim = min(lim, last_key_at_or_before(p.mask, p.P, p.blk, kb, token_pos(p.mask, p.P, p.blk, qb, my_row)));
+    const int q_first = qt * QT, q_last = min(q_first + QT, q_len) - 1;
+    auto last_key = [&](int qrow) {
+      return last_key_at_or_before(p.mask, p.P, p.blk, p.rem, kb, token_pos(p.mask, p.P, p.blk, p.rem, qb, qrow));
+    };
+    kv_vis = last_key(q_last) + 1;
+    kv_all = last_key(q_first) + 1;
+    lim = min(lim, last_key(min(q_first + wave * 32 * G + lr, q_len - 1)));
     // Nothing visible and nothing to initialise or write: the state stays as it is.
     if (kv_vis == 0 && p.flags == (kLoadState | kStoreState)) return;
   }
@@ -197,8 +203,8 @@ void fold_bf16_kernel(const FoldParams p) {
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     const int row = qt * QT + wave * 32 * G + g * 32 + lr;
-    row_ok[g] = row < p.q_rows;
-    srow[g] = (int64_t)r * p.q_rows + (row_ok[g] ? row : p.q_rows - 1);
+    row_ok[g] = row < q_len;
+    srow[g] = (int64_t)p.q_row0[r] + (row_ok[g] ? row : q_len - 1);
     st_row[g] = ((int64_t)bi * p.H + hi) * p.st_bh + srow[g];
   }
 
@@ -246,7 +252,7 @@ void fold_bf16_kernel(const FoldParams p) {
   const __bf16* kbase = (const __bf16*)p.k + bi * p.k_sb + hi * p.k_sh + p.k_off[r];
   const __bf16* vbase = (const __bf16*)p.v + bi * p.v_sb + hi * p.v_sh + p.v_off[r];
   // Tiles [0, n_plain) need no mask; tiles [n_plain, n_kt) compare keys with lim.
-  const int n_plain = min(kv_all, p.kv_rows) / TK;
+  const int n_plain = min(kv_all, kv_len) / TK;
   const int n_kt = (kv_vis + TK - 1) / TK;
   const float c2 = p.scale_log2;
 
@@ -266,7 +272,7 @@ void fold_bf16_kernel(const FoldParams p) {
     const int key0 = kt * TK;
     __bf16* kl = lds + buf * 2 * TE + wave * CPW * 512;
     __bf16* vl = kl + TE;
-    if (key0 + TK <= p.kv_rows) {
+    if (key0 + TK <= kv_len) {
       const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + (int64_t)key0 * k_sr);
       const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + (int64_t)key0 * v_sr);
 #pragma unroll
@@ -280,7 +286,7 @@ void fold_bf16_kernel(const FoldParams p) {
         const int u = (wave * CPW + j) * 64 + lane;
         const int lrow = u / UPR;
         const int gunit = (u % UPR) ^ swz<D>(lrow);
-        const int64_t g = min(key0 + lrow, p.kv_rows - 1);
+        const int64_t g = min(key0 + lrow, kv_len - 1);
         gload_lds16(kbase + g * k_sr + gunit * 8, kl + j * 512);
         gload_lds16(vbase + g * v_sr + gunit * 8, vl + j * 512);
       }

@@ -48,22 +48,26 @@ __global__ __launch_bounds__(256) void fold_f32_kernel(const FoldParams p) {
   const int tid = threadIdx.x;
   const int sub = tid % TPR;
   const int row = qt * ROWS + tid / TPR;
-  const bool row_ok = row < p.q_rows;
+  // This resident's block lengths; a query tile past its end has nothing to do.
+  const int q_len = p.q_len[r], kv_len = p.kv_len[r];
+  if (qt * ROWS >= q_len) return;
+  const bool row_ok = row < q_len;
 
   // Keys [0, kv_vis) are visible to some row of this workgroup; key c is
   // visible to this thread's row iff c <= lim.
-  int kv_vis = p.kv_rows;
-  int lim = p.kv_rows - 1;
+  int kv_vis = kv_len;
+  int lim = kv_len - 1;
   if (p.mask != kMaskNone) {
     const int qb = p.q_blk[r], kb = p.kv_blk[r];
-    const int q_last = min(qt * ROWS + ROWS, p.q_rows) - 1;
-    kv_vis = last_key_at_or_before(p.mask, p.P, p.blk, kb, token_pos(p.mask, p.P, p.blk, qb, q_last)) + 1;
-    const int my_row = min(row, p.q_rows - 1);
-    lim = min(lim, last_key_at_or_before(p.mask, p.P, p.blk, kb, token_pos(p.mask, p.P, p.blk, qb, my_row)));
+    auto last_key = [&](int qrow) {
+      return last_key_at_or_before(p.mask, p.P, p.blk, p.rem, kb, token_pos(p.mask, p.P, p.blk, p.rem, qb, qrow));
+    };
+    kv_vis = last_key(min(qt * ROWS + ROWS, q_len) - 1) + 1;
+    lim = min(lim, last_key(min(row, q_len - 1)));
     // Nothing visible and nothing to initialise or write: the state stays as it is.
     if (kv_vis == 0 && p.flags == (kLoadState | kStoreState)) return;
   }
-  const int64_t srow = (int64_t)r * p.q_rows + (row_ok ? row : p.q_rows - 1);
+  const int64_t srow = (int64_t)p.q_row0[r] + (row_ok ? row : q_len - 1);
   const int col0 = 64 * sub;
 
   float qv[64];
@@ -110,7 +114,7 @@ __global__ __launch_bounds__(256) void fold_f32_kernel(const FoldParams p) {
     for (int ch = tid; ch < kTileK * C4; ch += 256) {
       const int rr = ch / C4;
       const int cc = (ch % C4) * 4;
-      const int64_t g = min(key0 + rr, p.kv_rows - 1);
+      const int64_t g = min(key0 + rr, kv_len - 1);
       *(f32x4*)(ks + rr * D + cc) = *(const f32x4*)(kbase + g * p.k_sr + cc);
       *(f32x4*)(vs + rr * D + cc) = *(const f32x4*)(vbase + g * p.v_sr + cc);
     }

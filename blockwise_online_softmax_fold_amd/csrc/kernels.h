@@ -17,11 +17,12 @@ enum FoldFlags : int {
   kWriteOut = 4,    // write O = o / l to `out` instead (the last step of the ring)
 };
 
-// One fold launch: n_res resident query blocks, each of q_rows rows, each
-// folding its own visiting block of kv_rows rows.  Offsets and strides are in
-// elements.  Resident r's query rows start at row r * q_rows of q and of out;
-// its state row `row` is (bi * H + hi) * st_bh + r * q_rows + row of m and l
-// (times d for o); its visiting block starts at k + k_off[r] / v + v_off[r].
+// One fold launch: n_res resident query blocks; resident r has q_len[r] query
+// rows and folds its own visiting block of kv_len[r] rows (q_rows is the
+// largest q_len, which sizes the grid).  Offsets and strides are in elements.
+// Resident r's query rows start at row q_row0[r] of q and of out; its state
+// row `row` is (bi * H + hi) * st_bh + q_row0[r] + row of m and l (times d
+// for o); its visiting block starts at k + k_off[r] / v + v_off[r].
 struct FoldParams {
   const void* q;
   const void* k;
@@ -37,16 +38,20 @@ struct FoldParams {
   int64_t st_bh;  // rows per (batch, head) in the state arrays
   int64_t k_off[kMaxResident];
   int64_t v_off[kMaxResident];
+  int32_t q_len[kMaxResident];
+  int32_t kv_len[kMaxResident];
+  int64_t q_row0[kMaxResident];
   int32_t B, H, n_res;
-  int32_t q_rows, kv_rows;
+  int32_t q_rows;
   int32_t flags;
   float scale_log2;  // softmax scale times log2(e): scores are exponentiated in base 2
   // Causal masking (mask != kMaskNone): query row r of resident r_ and key row c
   // of its visiting block sit at sequence positions pos(q_blk[r_], r) and
-  // pos(kv_blk[r_], c) of a P-device ring with blocks of `blk` rows; keys after
-  // the query are masked.
+  // pos(kv_blk[r_], c) of a P-device ring over N = P blk + rem tokens (device
+  // j's block holds blk rows, one more when j < rem); keys after the query are
+  // masked.
   int32_t mask;
-  int32_t P, blk;
+  int32_t P, blk, rem;
   int32_t q_blk[kMaxResident];
   int32_t kv_blk[kMaxResident];
 };
@@ -54,26 +59,31 @@ struct FoldParams {
 // Masking modes (the token layout of the ring when causal).
 enum MaskMode : int {
   kMaskNone = 0,
-  kMaskContiguous = 1,  // device j holds tokens [j b, (j + 1) b)
+  kMaskContiguous = 1,  // device j holds the next run of tokens after device j - 1
   kMaskStriped = 2,     // device j holds tokens j, j + P, j + 2P, ...
-  kMaskZigzag = 3,      // device j holds chunks j and 2P - 1 - j of b / 2 tokens
+  kMaskZigzag = 3,      // device j holds chunks j and 2P - 1 - j of b / 2 tokens (rem = 0)
 };
 
-// Sequence position of row r of device j's block (blocks of b rows, P devices).
-__host__ __device__ inline int32_t token_pos(int mode, int32_t P, int32_t b, int32_t j, int32_t r) {
+// Rows of device j's block and, for the contiguous split, its first position.
+__host__ __device__ inline int32_t block_len(int32_t b, int32_t rem, int32_t j) { return b + (j < rem ? 1 : 0); }
+__host__ __device__ inline int32_t block_start(int32_t b, int32_t rem, int32_t j) { return j * b + (j < rem ? j : rem); }
+
+// Sequence position of row r of device j's block.
+__host__ __device__ inline int32_t token_pos(int mode, int32_t P, int32_t b, int32_t rem, int32_t j, int32_t r) {
   if (mode == kMaskStriped) return r * P + j;
   if (mode == kMaskZigzag) {
     const int32_t h = b >> 1;
     return r < h ? j * h + r : (2 * P - 1 - j) * h + (r - h);
   }
-  return j * b + r;
+  return block_start(b, rem, j) + r;
 }
 
 // Every layout numbers the rows of a block in increasing position (zig-zag:
 // chunk j < P comes before its mirror 2P - 1 - j), so the keys of device j's
 // block at or before a position x are a prefix of the block.  Largest such key
 // row (-1 if none).
-__host__ __device__ inline int32_t last_key_at_or_before(int mode, int32_t P, int32_t b, int32_t j, int32_t x) {
+__host__ __device__ inline int32_t last_key_at_or_before(int mode, int32_t P, int32_t b, int32_t rem, int32_t j,
+                                                        int32_t x) {
   int32_t c;
   if (mode == kMaskStriped) {
     c = x < j ? -1 : (x - j) / P;
@@ -85,10 +95,11 @@ __host__ __device__ inline int32_t last_key_at_or_before(int mode, int32_t P, in
     else
       c = x - j * h < h ? x - j * h : h - 1;
   } else {
-    c = x - j * b;
+    c = x - block_start(b, rem, j);
   }
   if (c < -1) c = -1;
-  return c < b - 1 ? c : b - 1;
+  const int32_t n = block_len(b, rem, j);
+  return c < n - 1 ? c : n - 1;
 }
 
 // Each launcher returns the launch status (hipGetLastError after the launch).

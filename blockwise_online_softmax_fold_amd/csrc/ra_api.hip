@@ -135,11 +135,29 @@ ra_status_t get_dev(DevRes** out) {
 constexpr size_t kAlign = 256;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// Blocks of the ring: N = P b + rem tokens; device j's block holds
+// block_len(b, rem, j) rows (b, one more for j < rem) starting at row
+// block_start(b, rem, j) of the sequence.
+struct Blocks {
+  int64_t b = 0, rem = 0, b_max = 0;
+  int64_t len(int64_t j) const { return ra::block_len((int32_t)b, (int32_t)rem, (int32_t)j); }
+  int64_t start(int64_t j) const { return ra::block_start((int32_t)b, (int32_t)rem, (int32_t)j); }
+};
+
+Blocks ring_blocks(int64_t N, int32_t P) {
+  Blocks k;
+  k.b = N / P;
+  k.rem = N % P;
+  k.b_max = k.b + (k.rem ? 1 : 0);
+  return k;
+}
+
 // Workspace of the ring driver: state of the n_q resident blocks
-// (m, l: [B, H, n_q*b]; o: [B, H, n_q*b, d]) followed by the K and V halves
-// of the double buffer, each [slot][n_q][B][H][b][d].
+// (m, l: [B, H, rows]; o: [B, H, rows, d], rows = the residents' rows, at most
+// n_q * b_max) followed by the K and V halves of the double buffer, each
+// [slot][n_q][B][H][b_max][d].
 struct RingLayout {
-  int64_t b = 0, rows = 0;
+  Blocks blk;
   int nslots = 0;
   size_t off_m = 0, off_l = 0, off_o = 0, off_k = 0, off_v = 0, total = 0;
   int64_t res_elems = 0;   // K (or V) elements of one resident block's slot
@@ -148,15 +166,15 @@ struct RingLayout {
 
 RingLayout ring_layout(ra_dtype_t dt, int64_t B, int64_t H, int64_t N, int64_t d, int32_t P, int32_t n_q) {
   RingLayout L;
-  L.b = N / P;
-  L.rows = (int64_t)n_q * L.b;
+  L.blk = ring_blocks(N, P);
+  const int64_t rows = (int64_t)n_q * L.blk.b_max;
   L.nslots = P - 1 < 2 ? P - 1 : 2;  // two visiting blocks, not P
-  const size_t st_rows = (size_t)B * H * L.rows;
+  const size_t st_rows = (size_t)B * H * rows;
   L.off_m = 0;
   L.off_l = round_up(L.off_m + st_rows * 4);
   L.off_o = round_up(L.off_l + st_rows * 4);
   L.off_k = round_up(L.off_o + st_rows * (size_t)d * 4);
-  L.res_elems = B * H * L.b * d;
+  L.res_elems = B * H * L.blk.b_max * d;
   L.slot_elems = L.res_elems * n_q;
   const size_t buf = (size_t)L.nslots * L.slot_elems * esize(dt);
   L.off_v = round_up(L.off_k + buf);
@@ -172,8 +190,7 @@ ra_status_t check_ring(const void* q, const int64_t* q_strides, const void* k, c
   if (st != RA_OK) return st;
   if (P < 1) return fail(RA_E_INVALID_ARG, "P=%d must be >= 1", (int)P);
   if (N < P) return fail(RA_E_INVALID_ARG, "N=%lld must be >= P=%d", (long long)N, (int)P);
-  if (N % P != 0) return fail(RA_E_UNSUPPORTED, "N=%lld is not a multiple of P=%d", (long long)N, (int)P);
-  if (N / P > 0x7fffffffLL / 4) return fail(RA_E_UNSUPPORTED, "block size N/P is too large");
+  if (N / P + 1 > 0x7fffffffLL / 4) return fail(RA_E_UNSUPPORTED, "block size N/P is too large");
   if (n_q < 1) return fail(RA_E_INVALID_ARG, "n_q=%d must be >= 1", (int)n_q);
   if (query_blocks == nullptr && n_q != P)
     return fail(RA_E_INVALID_ARG, "query_blocks is NULL (all blocks) but n_q=%d != P=%d", (int)n_q, (int)P);
@@ -197,30 +214,31 @@ void set_strides(int64_t* dst_b, int64_t* dst_h, int64_t* dst_r, const int64_t* 
   *dst_r = s[2];
 }
 
-// Copy block j of src ([B, H, N, d] with strides s) into a contiguous
-// [B, H, b, d] region at dst (the hand-off of one visiting block).
-ra_status_t copy_block(void* dst, const void* src, const int64_t* s, int64_t B, int64_t H, int64_t b, int64_t d,
-                       int64_t j, size_t es, hipStream_t stream) {
+// Copy rows [start, start + n) of src ([B, H, N, d] with strides s) into dst,
+// laid out [B][H][b_max][d] (the hand-off of one visiting block).
+ra_status_t copy_block(void* dst, const void* src, const int64_t* s, int64_t B, int64_t H, int64_t start, int64_t n,
+                       int64_t b_max, int64_t d, size_t es, hipStream_t stream) {
   const char* sp = (const char*)src;
   char* dp = (char*)dst;
   const size_t row_bytes = (size_t)d * es;
-  const size_t blk_bytes = (size_t)b * row_bytes;
+  const size_t blk_bytes = (size_t)n * row_bytes;
+  const size_t dst_head = (size_t)b_max * row_bytes;
   if (s[2] == d && (H == 1 || s[1] * (int64_t)es >= (int64_t)blk_bytes)) {
     // rows of a block are contiguous: one 2-D copy over heads per batch
     const size_t spitch = H == 1 ? blk_bytes : (size_t)s[1] * es;
     for (int64_t bi = 0; bi < B; ++bi) {
-      const char* from = sp + (size_t)(bi * s[0] + j * b * d) * es;
-      char* to = dp + (size_t)bi * H * blk_bytes;
-      RA_HIP(hipMemcpy2DAsync(to, blk_bytes, from, spitch, blk_bytes, (size_t)H, hipMemcpyDeviceToDevice, stream),
+      const char* from = sp + (size_t)(bi * s[0] + start * d) * es;
+      char* to = dp + (size_t)bi * H * dst_head;
+      RA_HIP(hipMemcpy2DAsync(to, dst_head, from, spitch, blk_bytes, (size_t)H, hipMemcpyDeviceToDevice, stream),
              "hipMemcpy2DAsync (hand-off)");
     }
     return RA_OK;
   }
   for (int64_t bi = 0; bi < B; ++bi)
     for (int64_t hi = 0; hi < H; ++hi) {
-      const char* from = sp + (size_t)(bi * s[0] + hi * s[1] + j * b * s[2]) * es;
-      char* to = dp + (size_t)(bi * H + hi) * blk_bytes;
-      RA_HIP(hipMemcpy2DAsync(to, row_bytes, from, (size_t)s[2] * es, row_bytes, (size_t)b, hipMemcpyDeviceToDevice,
+      const char* from = sp + (size_t)(bi * s[0] + hi * s[1] + start * s[2]) * es;
+      char* to = dp + (size_t)(bi * H + hi) * dst_head;
+      RA_HIP(hipMemcpy2DAsync(to, row_bytes, from, (size_t)s[2] * es, row_bytes, (size_t)n, hipMemcpyDeviceToDevice,
                               stream),
              "hipMemcpy2DAsync (hand-off)");
     }
@@ -291,7 +309,8 @@ namespace {
 ra_status_t fold_block_impl(const void* q, const int64_t q_strides[3], const void* k, const int64_t k_strides[3],
                             const void* v, const int64_t v_strides[3], ra_dtype_t dt, int64_t B, int64_t H,
                             int64_t q_rows, int64_t kv_rows, int64_t d, float scale, float* m, float* l, float* o,
-                            int mask, int32_t P, int32_t q_block, int32_t kv_block, void* stream) {
+                            int mask, int32_t P, int32_t blk, int32_t rem, int32_t q_block, int32_t kv_block,
+                            void* stream) {
   ra_status_t st = check_common(dt, B, H, d);
   if (st != RA_OK) return st;
   if (q_rows < 0 || kv_rows < 0) return fail(RA_E_INVALID_ARG, "q_rows and kv_rows must be >= 0");
@@ -326,12 +345,15 @@ ra_status_t fold_block_impl(const void* q, const int64_t q_strides[3], const voi
   p.H = (int32_t)H;
   p.n_res = 1;
   p.q_rows = (int32_t)q_rows;
-  p.kv_rows = (int32_t)kv_rows;
+  p.q_len[0] = (int32_t)q_rows;
+  p.kv_len[0] = (int32_t)kv_rows;
+  p.q_row0[0] = 0;
   p.flags = ra::kLoadState | ra::kStoreState;
   p.scale_log2 = to_log2_scale(sc);
   p.mask = mask;
   p.P = P;
-  p.blk = (int32_t)kv_rows;
+  p.blk = blk;
+  p.rem = rem;
   p.q_blk[0] = q_block;
   p.kv_blk[0] = kv_block;
   RA_HIP(launch_fold(p, dt, (int)d, (hipStream_t)stream), "fold launch");
@@ -343,13 +365,15 @@ bool valid_layout(int layout) {
          layout == RA_CAUSAL_ZIGZAG;
 }
 
-// Positions of a causal ring (P blocks of b rows) must fit the kernels' int32.
-ra_status_t check_causal(int layout, int64_t P, int64_t b) {
+// Positions of a causal ring over N tokens must fit the kernels' int32; the
+// zig-zag split cuts the sequence into 2P equal chunks.
+ra_status_t check_causal(int layout, int64_t P, int64_t N) {
   if (!valid_layout(layout)) return fail(RA_E_INVALID_ARG, "unknown causal layout %d", layout);
   if (layout == RA_CAUSAL_NONE) return RA_OK;
-  if (P * b > 0x7fffffffLL) return fail(RA_E_UNSUPPORTED, "P*b=%lld positions do not fit 32 bits", (long long)(P * b));
-  if (layout == RA_CAUSAL_ZIGZAG && b % 2 != 0)
-    return fail(RA_E_INVALID_ARG, "zig-zag layout needs an even block size, got %lld", (long long)b);
+  if (N > 0x7fffffffLL) return fail(RA_E_UNSUPPORTED, "N=%lld positions do not fit 32 bits", (long long)N);
+  if (layout == RA_CAUSAL_ZIGZAG && N % (2 * P) != 0)
+    return fail(RA_E_INVALID_ARG, "zig-zag layout needs N a multiple of 2P, got N=%lld, P=%lld", (long long)N,
+                (long long)P);
   return RA_OK;
 }
 
@@ -361,27 +385,27 @@ RA_API ra_status_t ra_fold_block(const void* q, const int64_t q_strides[3], cons
                                  float* o, void* stream) {
   g_err.clear();
   return fold_block_impl(q, q_strides, k, k_strides, v, v_strides, dt, B, H, q_rows, kv_rows, d, scale, m, l, o,
-                         ra::kMaskNone, 1, 0, 0, stream);
+                         ra::kMaskNone, 1, (int32_t)kv_rows, 0, 0, 0, stream);
 }
 
 RA_API ra_status_t ra_fold_block_causal(const void* q, const int64_t q_strides[3], const void* k,
                                         const int64_t k_strides[3], const void* v, const int64_t v_strides[3],
-                                        ra_dtype_t dt, int64_t B, int64_t H, int64_t rows, int64_t d, float scale,
+                                        ra_dtype_t dt, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
                                         ra_causal_t layout, int32_t P, int32_t q_block, int32_t kv_block, float* m,
                                         float* l, float* o, void* stream) {
   g_err.clear();
   ra_status_t st;
   if (!valid_layout((int)layout)) return fail(RA_E_INVALID_ARG, "unknown causal layout %d", (int)layout);
-  if (layout != RA_CAUSAL_NONE) {
-    if (P < 1) return fail(RA_E_INVALID_ARG, "P=%d must be >= 1", (int)P);
-    if (q_block < 0 || q_block >= P || kv_block < 0 || kv_block >= P)
-      return fail(RA_E_INVALID_ARG, "q_block=%d and kv_block=%d must lie in [0, P=%d)", (int)q_block, (int)kv_block,
-                  (int)P);
-    if (rows < 0) return fail(RA_E_INVALID_ARG, "rows=%lld must be >= 0", (long long)rows);
-    if ((st = check_causal((int)layout, P, rows)) != RA_OK) return st;
-  }
-  return fold_block_impl(q, q_strides, k, k_strides, v, v_strides, dt, B, H, rows, rows, d, scale, m, l, o,
-                         (int)layout, P, q_block, kv_block, stream);
+  if (P < 1) return fail(RA_E_INVALID_ARG, "P=%d must be >= 1", (int)P);
+  if (N < P) return fail(RA_E_INVALID_ARG, "N=%lld must be >= P=%d", (long long)N, (int)P);
+  if (q_block < 0 || q_block >= P || kv_block < 0 || kv_block >= P)
+    return fail(RA_E_INVALID_ARG, "q_block=%d and kv_block=%d must lie in [0, P=%d)", (int)q_block, (int)kv_block,
+                (int)P);
+  if (N / P + 1 > 0x7fffffffLL / 4) return fail(RA_E_UNSUPPORTED, "block size N/P is too large");
+  if ((st = check_causal((int)layout, P, N)) != RA_OK) return st;
+  const Blocks bk = ring_blocks(N, P);
+  return fold_block_impl(q, q_strides, k, k_strides, v, v_strides, dt, B, H, bk.len(q_block), bk.len(kv_block), d,
+                         scale, m, l, o, (int)layout, P, (int32_t)bk.b, (int32_t)bk.rem, q_block, kv_block, stream);
 }
 
 RA_API ra_status_t ra_finalize(const float* l, const float* o, void* out, const int64_t out_strides[3],
@@ -403,8 +427,8 @@ RA_API ra_status_t ra_finalize(const float* l, const float* o, void* out, const 
 RA_API size_t ra_ring_workspace_bytes(ra_dtype_t dt, int64_t B, int64_t H, int64_t N, int64_t d, int32_t P,
                                       int32_t n_q) {
   const std::string saved = g_err;
-  const bool ok = check_common(dt, B, H, d) == RA_OK && P >= 1 && N >= P && N % P == 0 && n_q >= 1 &&
-                  N / P <= 0x7fffffffLL / 4;
+  const bool ok = check_common(dt, B, H, d) == RA_OK && P >= 1 && N >= P && n_q >= 1 &&
+                  N / P + 1 <= 0x7fffffffLL / 4;
   g_err = saved;
   if (!ok) return 0;
   return ring_layout(dt, B, H, N, d, P, n_q).total;
@@ -420,7 +444,7 @@ ra_status_t ring_forward_impl(const void* q, const int64_t q_strides[3], const v
   ra_status_t st = check_ring(q, q_strides, k, k_strides, v, v_strides, out, out_strides, dt, B, H, N, d, P,
                               query_blocks, n_q);
   if (st != RA_OK) return st;
-  if ((st = check_causal(mask, P, N / P)) != RA_OK) return st;
+  if ((st = check_causal(mask, P, N)) != RA_OK) return st;
   float sc;
   if ((st = resolve_scale(scale, d, &sc)) != RA_OK) return st;
   const RingLayout L = ring_layout(dt, B, H, N, d, P, n_q);
@@ -432,6 +456,11 @@ ra_status_t ring_forward_impl(const void* q, const int64_t q_strides[3], const v
       return fail(RA_E_INVALID_ARG, "workspace is not %zu-byte aligned", kAlign);
   }
   auto qb = [&](int32_t r) { return query_blocks ? query_blocks[r] : r; };
+  const Blocks& bk = L.blk;
+  // Resident r's rows start at row_of[r] of q, out and the state.
+  std::vector<int64_t> row_of(n_q + 1, 0);
+  for (int32_t r = 0; r < n_q; ++r) row_of[r + 1] = row_of[r] + bk.len(qb(r));
+  const int64_t rows = row_of[n_q];
 
   hipStream_t stream = (hipStream_t)stream_;
   DevRes* dr = nullptr;
@@ -448,7 +477,7 @@ ra_status_t ring_forward_impl(const void* q, const int64_t q_strides[3], const v
   char* kbuf = base + L.off_k;
   char* vbuf = base + L.off_v;
   const size_t es = esize(dt);
-  const int64_t b = L.b;
+  const int64_t bm = bk.b_max;
 
   const bool serial = env_flag("RA_SYNC_EACH_STEP");
   hipStream_t side = serial ? stream : dr->side;
@@ -470,8 +499,8 @@ ra_status_t ring_forward_impl(const void* q, const int64_t q_strides[3], const v
         const int64_t jj = j < 0 ? j + P : j;
         char* kd = kbuf + ((size_t)s * L.slot_elems + (size_t)r * L.res_elems) * es;
         char* vd = vbuf + ((size_t)s * L.slot_elems + (size_t)r * L.res_elems) * es;
-        if ((st = copy_block(kd, k, k_strides, B, H, b, d, jj, es, side)) != RA_OK) return st;
-        if ((st = copy_block(vd, v, v_strides, B, H, b, d, jj, es, side)) != RA_OK) return st;
+        if ((st = copy_block(kd, k, k_strides, B, H, bk.start(jj), bk.len(jj), bm, d, es, side)) != RA_OK) return st;
+        if ((st = copy_block(vd, v, v_strides, B, H, bk.start(jj), bk.len(jj), bm, d, es, side)) != RA_OK) return st;
       }
       if (!serial) RA_HIP(hipEventRecord(dr->ready[s], side), "hipEventRecord");
     }
@@ -480,46 +509,51 @@ ra_status_t ring_forward_impl(const void* q, const int64_t q_strides[3], const v
     for (int32_t r0 = 0; r0 < n_q; r0 += ra::kMaxResident) {
       const int32_t nr = n_q - r0 < ra::kMaxResident ? n_q - r0 : ra::kMaxResident;
       FoldParams p = {};
-      p.q = (const char*)q + (size_t)r0 * b * q_strides[2] * es;
-      p.out = (char*)out + (size_t)r0 * b * out_strides[2] * es;
-      p.m = m + (size_t)r0 * b;
-      p.l = l + (size_t)r0 * b;
-      p.o = o + (size_t)r0 * b * d;
+      p.q = (const char*)q + (size_t)row_of[r0] * q_strides[2] * es;
+      p.out = (char*)out + (size_t)row_of[r0] * out_strides[2] * es;
+      p.m = m + row_of[r0];
+      p.l = l + row_of[r0];
+      p.o = o + (size_t)row_of[r0] * d;
       set_strides(&p.q_sb, &p.q_sh, &p.q_sr, q_strides);
       set_strides(&p.out_sb, &p.out_sh, &p.out_sr, out_strides);
-      p.st_bh = L.rows;
+      p.st_bh = rows;
       if (t == 0) {  // the own block, read in place
         p.k = k;
         p.v = v;
         set_strides(&p.k_sb, &p.k_sh, &p.k_sr, k_strides);
         set_strides(&p.v_sb, &p.v_sh, &p.v_sr, v_strides);
         for (int32_t r = 0; r < nr; ++r) {
-          p.k_off[r] = (int64_t)qb(r0 + r) * b * k_strides[2];
-          p.v_off[r] = (int64_t)qb(r0 + r) * b * v_strides[2];
+          p.k_off[r] = bk.start(qb(r0 + r)) * k_strides[2];
+          p.v_off[r] = bk.start(qb(r0 + r)) * v_strides[2];
         }
       } else {
         const int s = slot_of(t);
         p.k = kbuf + (size_t)s * L.slot_elems * es;
         p.v = vbuf + (size_t)s * L.slot_elems * es;
-        p.k_sb = p.v_sb = H * b * d;
-        p.k_sh = p.v_sh = b * d;
+        p.k_sb = p.v_sb = H * bm * d;
+        p.k_sh = p.v_sh = bm * d;
         p.k_sr = p.v_sr = d;
         for (int32_t r = 0; r < nr; ++r) p.k_off[r] = p.v_off[r] = (int64_t)(r0 + r) * L.res_elems;
       }
       p.B = (int32_t)B;
       p.H = (int32_t)H;
       p.n_res = nr;
-      p.q_rows = (int32_t)b;
-      p.kv_rows = (int32_t)b;
       p.flags = (t == 0 ? 0 : ra::kLoadState) | (t == P - 1 ? ra::kWriteOut : ra::kStoreState);
       p.scale_log2 = to_log2_scale(sc);
       p.mask = mask;
       p.P = P;
-      p.blk = (int32_t)b;
+      p.blk = (int32_t)bk.b;
+      p.rem = (int32_t)bk.rem;
+      p.q_rows = 0;
       for (int32_t r = 0; r < nr; ++r) {
         const int32_t i = qb(r0 + r);
+        const int32_t j = (int32_t)(((int64_t)i - t) % P + P) % P;
         p.q_blk[r] = i;
-        p.kv_blk[r] = (int32_t)(((int64_t)i - t) % P + P) % P;
+        p.kv_blk[r] = j;
+        p.q_len[r] = (int32_t)bk.len(i);
+        p.kv_len[r] = (int32_t)bk.len(j);
+        p.q_row0[r] = row_of[r0 + r] - row_of[r0];
+        if (p.q_len[r] > p.q_rows) p.q_rows = p.q_len[r];
       }
       const long pi = prof_begin(stream);
       RA_HIP(launch_fold(p, dt, (int)d, stream), "fold launch");

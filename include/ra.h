@@ -64,9 +64,10 @@ typedef enum { RA_DTYPE_F32 = 0, RA_DTYPE_BF16 = 1 } ra_dtype_t;
  * or before its own position (math page, "Causal masking, load balance, and
  * other wrinkles"; bembew.net "Implementation Considerations", causal
  * masking).  The ring's N = P*b tokens are dealt to the P devices in one of
- * three ways (vibeengines.com, "The causal-mask catch"); row r (0 <= r < b) of
- * device j's block holds sequence position
- *   RA_CAUSAL_CONTIGUOUS: j*b + r                     (contiguous split)
+ * three ways (vibeengines.com, "The causal-mask catch"); row r of device j's
+ * block (b = N/P rows when P divides N; see "Blocks of the ring") holds
+ * sequence position
+ *   RA_CAUSAL_CONTIGUOUS: start_j + r, start_j = j*b + min(j, N mod P)
  *   RA_CAUSAL_STRIPED:    r*P + j                     (round-robin, "striped")
  *   RA_CAUSAL_ZIGZAG:     j*h + r          for r < h  (h = b/2: chunk j and its
  *                         (2P-1-j)*h + r-h for r >= h  mirror chunk 2P-1-j)
@@ -116,17 +117,18 @@ ra_status_t ra_fold_block(const void* q, const int64_t q_strides[3], const void*
 /*
  * ra_fold_block_causal -- ra_fold_block under a causal mask: the query block
  * is device q_block's and the visiting block device kv_block's of a P-device
- * ring in the given layout, both of b = rows rows (so q and k, v have the
- * same row count), 0 <= q_block, kv_block < P.  Arguments and state as for
- * ra_fold_block.  RA_CAUSAL_ZIGZAG needs rows even; P*rows must stay below
- * 2^31.  layout RA_CAUSAL_NONE is exactly ra_fold_block with q_rows = kv_rows
- * = rows (P, q_block, kv_block are then ignored).  A pair with no visible key
- * (for instance kv_block > q_block in the contiguous layout) leaves the state
- * bit for bit as it was.
+ * ring over N tokens in the given layout, 0 <= q_block, kv_block < P.  The
+ * blocks' row counts follow from N and P (see "Blocks of the ring" below): q
+ * and the state hold block q_block's rows, k and v block kv_block's.
+ * Arguments and state otherwise as for ra_fold_block.  RA_CAUSAL_ZIGZAG needs
+ * N a multiple of 2P; N must stay below 2^31.  layout RA_CAUSAL_NONE folds the
+ * same two blocks without a mask.  A pair with no visible key (for instance
+ * kv_block > q_block in the contiguous layout) leaves the state bit for bit as
+ * it was.
  */
 ra_status_t ra_fold_block_causal(const void* q, const int64_t q_strides[3], const void* k,
                                  const int64_t k_strides[3], const void* v, const int64_t v_strides[3],
-                                 ra_dtype_t dt, int64_t B, int64_t H, int64_t rows, int64_t d, float scale,
+                                 ra_dtype_t dt, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
                                  ra_causal_t layout, int32_t P, int32_t q_block, int32_t kv_block, float* m,
                                  float* l, float* o, void* stream);
 
@@ -139,6 +141,15 @@ ra_status_t ra_fold_block_causal(const void* q, const int64_t q_strides[3], cons
  */
 ra_status_t ra_finalize(const float* l, const float* o, void* out, const int64_t out_strides[3], ra_dtype_t out_dt,
                         int64_t B, int64_t H, int64_t rows, int64_t d, void* stream);
+
+/*
+ * Blocks of the ring.  N tokens are split over P devices, 1 <= P <= N.  When P
+ * divides N every block holds b = N/P rows; otherwise (bembew.net
+ * "Implementation Considerations": padding or dynamic partitioning) the first
+ * N mod P devices hold N/P + 1 rows and the others N/P, so block j starts at
+ * row j*(N/P) + min(j, N mod P).  Dealing tokens round-robin (the striped
+ * layout) gives exactly these sizes.
+ */
 
 /*
  * ra_ring_workspace_bytes -- device workspace ra_ring_forward needs: the fp32
@@ -155,10 +166,12 @@ size_t ra_ring_workspace_bytes(ra_dtype_t dt, int64_t B, int64_t H, int64_t N, i
  * Math page, "Sharding the sequence", "The ring schedule", "Accumulation math,
  * step by step"; bembew.net "Conceptual Algorithm".
  *
- * q:   [B, H, n_q*b, d] -- the resident query blocks stacked along rows in
- *      query_blocks order (b = N/P); strides q_strides.
- * k,v: [B, H, N, d] -- the whole sequence; block j is rows [j*b, (j+1)*b).
- * out: [B, H, n_q*b, d] -- like q; receives O_i = o / l.
+ * q:   [B, H, rows, d] -- the resident query blocks stacked along rows in
+ *      query_blocks order (rows = the sum of their block sizes, n_q*N/P when P
+ *      divides N); strides q_strides.
+ * k,v: [B, H, N, d] -- the whole sequence; block j is its rows as given under
+ *      "Blocks of the ring" (rows [j*b, (j+1)*b) when P divides N).
+ * out: [B, H, rows, d] -- like q; receives O_i = o / l.
  * query_blocks: HOST array of n_q block ids in [0, P); NULL means 0..P-1
  *      (then n_q must equal P).
  * On step t resident block i folds block (i - t) mod P.  Step 0 reads the own
@@ -170,7 +183,6 @@ size_t ra_ring_workspace_bytes(ra_dtype_t dt, int64_t B, int64_t H, int64_t N, i
  *      256-byte aligned, or NULL to let the library allocate and free one in
  *      stream order.  Two calls that share a workspace must be ordered on
  *      their streams.
- * N % P != 0 returns RA_E_UNSUPPORTED.
  */
 ra_status_t ra_ring_forward(const void* q, const int64_t q_strides[3], const void* k, const int64_t k_strides[3],
                             const void* v, const int64_t v_strides[3], void* out, const int64_t out_strides[3],
@@ -180,10 +192,11 @@ ra_status_t ra_ring_forward(const void* q, const int64_t q_strides[3], const voi
 
 /*
  * ra_ring_forward_causal -- ra_ring_forward under a causal mask.  q, k, v and
- * out are in the layout's device order: block j (rows [j*b, (j+1)*b)) is
- * device j's share, holding the positions given above for `layout`.  Every
- * other argument, the workspace and the schedule are those of
- * ra_ring_forward; RA_CAUSAL_ZIGZAG needs b even and N must stay below 2^31.
+ * out are in the layout's device order: block j is device j's share, holding
+ * the positions given above for `layout` (contiguous: block j's first
+ * position is its first row's index in the sequence).  Every other argument,
+ * the workspace and the schedule are those of ra_ring_forward;
+ * RA_CAUSAL_ZIGZAG needs N a multiple of 2P and N must stay below 2^31.
  * Steps whose visiting block lies entirely in the resident block's future
  * fold nothing (the hand-off still moves the block, as the ring would).
  * Every row sees at least its own position, so no output row has l = 0.

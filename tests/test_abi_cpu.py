@@ -101,7 +101,6 @@ def _ring(lib, dt=BF16, B=1, H=32, N=131072, d=128, P=16, qb=None, n_q=16, scale
 
 
 @pytest.mark.parametrize("kwargs,status,needle", [
-    (dict(N=1000, P=16), 2, "not a multiple"),
     (dict(P=0), 1, "P=0"),
     (dict(N=8, P=16), 1, ">= P"),
     (dict(n_q=4), 1, "n_q=4 != P=16"),
@@ -130,7 +129,16 @@ def test_ring_workspace_is_two_blocks_not_P(lib):
         blocks = min(2, P - 1) * 2 * B * H * b * d * 2  # K and V, bf16
         assert state + blocks <= sizes[P] <= state + blocks + 5 * 256
     assert sizes[4] == sizes[16] == sizes[64]
-    assert lib.ra_ring_workspace_bytes(BF16, 1, 1, 1000, 128, 16, 1) == 0  # rejected shape
+    assert lib.ra_ring_workspace_bytes(BF16, 1, 1, 8, 128, 16, 1) == 0  # rejected shape: N < P
+
+
+def test_ring_workspace_uneven_blocks(lib):
+    """N not a multiple of P: every slot and state row is sized for the
+    longest block, N // P + 1 rows."""
+    B, H, d, n_q = 1, 2, 64, 3
+    even = lib.ra_ring_workspace_bytes(BF16, B, H, 16 * 4097, d, 16, n_q)
+    uneven = lib.ra_ring_workspace_bytes(BF16, B, H, 16 * 4096 + 5, d, 16, n_q)
+    assert uneven == even > 0
 
 
 def test_state_init_and_finalize_reject(lib):
@@ -141,8 +149,8 @@ def test_state_init_and_finalize_reject(lib):
     assert lib.ra_finalize(A, A, A, S_BF16, 9, 1, 1, 4, 64, None) == 1
 
 
-def _fold_causal(lib, layout=1, P=4, qb=0, kb=0, rows=1024, dt=BF16, d=128, q=A, k=A, m=A):
-    return lib.ra_fold_block_causal(q, S_BF16, k, S_BF16, A, S_BF16, dt, 1, 16, rows, d, ctypes.c_float(0.0),
+def _fold_causal(lib, layout=1, P=4, qb=0, kb=0, N=4096, dt=BF16, d=128, q=A, k=A, m=A):
+    return lib.ra_fold_block_causal(q, S_BF16, k, S_BF16, A, S_BF16, dt, 1, 16, N, d, ctypes.c_float(0.0),
                                     layout, P, qb, kb, m, A, A, None)
 
 
@@ -152,9 +160,9 @@ def _fold_causal(lib, layout=1, P=4, qb=0, kb=0, rows=1024, dt=BF16, d=128, q=A,
     (dict(P=0), 1, "P=0"),
     (dict(qb=4), 1, "must lie in [0, P=4)"),
     (dict(kb=-1), 1, "must lie in [0, P=4)"),
-    (dict(layout=3, rows=1023), 1, "even block size"),
-    (dict(layout=2, P=1 << 22, rows=1024), 2, "do not fit 32 bits"),
-    (dict(rows=-5), 1, "rows=-5"),
+    (dict(N=3), 1, "N=3 must be >= P=4"),
+    (dict(layout=3, N=4100), 1, "multiple of 2P"),
+    (dict(layout=2, P=1024, N=1 << 31), 2, "do not fit 32 bits"),
     (dict(q=ctypes.c_void_p(None)), 1, "q is NULL"),
     (dict(m=ctypes.c_void_p(None)), 1, "NULL"),
     (dict(d=80), 2, "head dim"),
@@ -164,13 +172,12 @@ def test_fold_block_causal_rejects(lib, kwargs, status, needle):
     assert needle in lib.ra_last_error().decode()
 
 
-def test_fold_block_causal_empty_and_none_layout_without_gpu(lib):
-    N = ctypes.c_void_p(None)
-    assert _fold_causal(lib, rows=0, q=N, k=N, m=N) == 0
-    assert _fold_causal(lib, layout=3, rows=0, q=N, k=N, m=N) == 0
-    # RA_CAUSAL_NONE ignores P and the block ids, like ra_fold_block
-    assert _fold_causal(lib, layout=0, P=0, qb=7, kb=-3, rows=0) == 0
-    assert lib.ra_last_error().decode() == ""
+def test_fold_block_causal_uneven_blocks_are_checked_on_host(lib):
+    # N = 4097 over P = 4: block 0 has 1025 rows, the others 1024 -- still host-side
+    # validation only: a NULL q is caught before any GPU work
+    assert _fold_causal(lib, N=4097, qb=0, kb=3, q=ctypes.c_void_p(None)) == 1
+    assert "q is NULL" in lib.ra_last_error().decode()
+    assert _fold_causal(lib, layout=0, N=4097, qb=1, kb=2, m=ctypes.c_void_p(None)) == 1
 
 
 def _ring_causal(lib, layout=1, N=131072, P=16, n_q=16, d=128):
@@ -180,8 +187,9 @@ def _ring_causal(lib, layout=1, N=131072, P=16, n_q=16, d=128):
 
 @pytest.mark.parametrize("kwargs,status,needle", [
     (dict(layout=4), 1, "unknown causal layout"),
-    (dict(layout=3, N=16 * 1001), 1, "even block size"),
-    (dict(layout=1, N=1000), 2, "not a multiple"),
+    (dict(layout=3, N=16 * 1001), 1, "multiple of 2P"),
+    (dict(layout=3, N=16 * 1000 + 3), 1, "multiple of 2P"),
+    (dict(layout=1, N=10), 1, ">= P"),
     (dict(layout=2, d=48), 2, "head dim"),
 ])
 def test_ring_forward_causal_rejects(lib, kwargs, status, needle):

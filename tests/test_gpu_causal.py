@@ -115,7 +115,7 @@ def test_fold_block_causal_none_layout_is_fold_block(ra, dtype):
         l, o = torch.empty_like(m), torch.empty((1, 3, 130, 128), device="cuda")
         ra.ra_state_init(m, l, o)
         if causal:
-            ra.ra_fold_block_causal(q, k, v, m, l, o, None, 0, 5, 9)
+            ra.ra_fold_block_causal(q, k, v, m, l, o, None, 1, 0, 0)
         else:
             ra.ra_fold_block(q, k, v, m, l, o)
         outs.append((m, l, o))
