@@ -21,18 +21,21 @@ Everything here is plain NumPy in float64, written from the pages:
 * ``block_bounds`` -- the rows of each device's block; when N is not a
   multiple of P the first N mod P blocks hold one row more (bembew.net
   "Implementation Considerations", load balancing).
+* ``backward`` -- dQ, dK, dV: the dense gradients and the ring backward in
+  which dK, dV accumulators travel with the blocks (vibeengines.com method
+  step 6).
 * ``layouts`` -- contiguous, striped and zig-zag token layouts and the causal
   positions they imply (math page "Causal masking, load balance, and other
   wrinkles"; vibeengines.com "The causal-mask catch").
 
 Every function here is pinned (``tests/test_oracle.py``, ``test_oracle_causal.py``,
-``test_oracle_ragged.py``) against values the
+``test_oracle_ragged.py``, ``test_oracle_backward.py``) against values the
 pages print (the worked two-block example), closed forms, a brute-force
 pure-Python evaluation, a library routine (torch's fp64 CPU attention) and
 invariants the pages state (order independence, P = 1).
 """
 
-from . import layouts
+from . import backward, layouts
 from .attention import dense_attention, dense_attention_rows
 from .ring import (
     State,
@@ -46,6 +49,7 @@ from .ring import (
 
 __all__ = [
     "State",
+    "backward",
     "block_bounds",
     "layouts",
     "dense_attention",
