@@ -10,7 +10,10 @@ include/ra.h); this package is its thin ctypes binding:
   with the double-buffered K/V hand-off on a side stream
 * ``ra_fold_block_causal``, ``ra_ring_forward_causal`` -- the same under a
   causal mask, for contiguous, striped or zig-zag token layouts
-* ``ra_ring_workspace_bytes``, ``ra_last_error``, ``ra_version``
+* ``ra_ring_forward_ex`` -- the forward that also returns each row's log-sum-exp
+* ``ra_ring_backward`` -- dQ, dK, dV on the same ring
+* ``ra_ring_workspace_bytes``, ``ra_ring_backward_workspace_bytes``,
+  ``ra_last_error``, ``ra_version``
 """
 
 from .binding import (
@@ -28,7 +31,10 @@ from .binding import (
     ra_profile_read,
     ra_last_error,
     ra_ring_forward,
+    ra_ring_backward,
+    ra_ring_backward_workspace_bytes,
     ra_ring_forward_causal,
+    ra_ring_forward_ex,
     ra_ring_workspace_bytes,
     ra_state_init,
     ra_version,
@@ -49,7 +55,10 @@ __all__ = [
     "ra_profile_read",
     "ra_last_error",
     "ra_ring_forward",
+    "ra_ring_backward",
+    "ra_ring_backward_workspace_bytes",
     "ra_ring_forward_causal",
+    "ra_ring_forward_ex",
     "ra_ring_workspace_bytes",
     "ra_state_init",
     "ra_version",

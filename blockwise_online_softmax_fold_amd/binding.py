@@ -40,6 +40,9 @@ EXPORTED = (
     "ra_ring_workspace_bytes",
     "ra_ring_forward",
     "ra_ring_forward_causal",
+    "ra_ring_forward_ex",
+    "ra_ring_backward_workspace_bytes",
+    "ra_ring_backward",
     "ra_last_error",
     "ra_version",
     "ra_profile_folds",
@@ -93,6 +96,16 @@ def load() -> ctypes.CDLL:
                                            i64, i64, i64, i32, ctypes.POINTER(ctypes.c_int32), i32, f32,
                                            ctypes.c_int, vp, sz, vp]
     lib.ra_ring_forward_causal.restype = ctypes.c_int
+    lib.ra_ring_forward_ex.argtypes = [vp, strides, vp, strides, vp, strides, vp, strides, vp, ctypes.c_int, i64, i64,
+                                       i64, i64, i32, ctypes.POINTER(ctypes.c_int32), i32, f32, ctypes.c_int, vp, sz,
+                                       vp]
+    lib.ra_ring_forward_ex.restype = ctypes.c_int
+    lib.ra_ring_backward_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i64, i64, i32, i32]
+    lib.ra_ring_backward_workspace_bytes.restype = sz
+    lib.ra_ring_backward.argtypes = [vp, strides, vp, strides, vp, strides, vp, strides, vp, strides, vp, vp, strides,
+                                     vp, strides, vp, strides, ctypes.c_int, i64, i64, i64, i64, i32,
+                                     ctypes.POINTER(ctypes.c_int32), i32, f32, ctypes.c_int, vp, sz, vp]
+    lib.ra_ring_backward.restype = ctypes.c_int
     lib.ra_last_error.argtypes = []
     lib.ra_last_error.restype = ctypes.c_char_p
     lib.ra_version.argtypes = []
@@ -258,13 +271,66 @@ def ra_ring_forward_causal(q, k, v, P: int, layout, query_blocks: Sequence[int] 
     return _ring(q, k, v, P, query_blocks, out, scale, workspace, stream, layout)
 
 
-def _ring(q, k, v, P, query_blocks, out, scale, workspace, stream, layout):
+def ra_ring_forward_ex(q, k, v, P: int, layout=None, query_blocks: Sequence[int] | None = None, out=None, lse=None,
+                       scale: float = 0.0, workspace=None, stream=None):
+    """The ring forward (causal when ``layout`` is given) that also returns each
+    resident row's log-sum-exp: (out, lse), lse float32 [B, H, rows]."""
+    import torch
+
+    if lse is None:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != tuple(q.shape[:3]):
+        raise ValueError("lse must be a contiguous float32 [B, H, rows] tensor")
+    out = _ring(q, k, v, P, query_blocks, out, scale, workspace, stream, layout, lse=lse)
+    return out, lse
+
+
+def ra_ring_backward_workspace_bytes(dtype, B: int, H: int, N: int, d: int, P: int, n_q: int) -> int:
+    import torch
+
+    code = RA_DTYPE_BF16 if dtype == torch.bfloat16 else RA_DTYPE_F32 if dtype == torch.float32 else -1
+    return int(load().ra_ring_backward_workspace_bytes(code, B, H, N, d, P, n_q))
+
+
+def ra_ring_backward(q, k, v, out, dout, lse, P: int, layout=None, query_blocks: Sequence[int] | None = None,
+                     dq=None, dk=None, dv=None, scale: float = 0.0, workspace=None, stream=None):
+    """Gradients on the ring: (dq, dk, dv).  q, k, v, P, layout, query_blocks and
+    scale as given to the forward; out, lse from ra_ring_forward_ex; dout like
+    out.  dk, dv hold the resident blocks' shares (full gradients when every
+    block is resident)."""
     import torch
 
     B, H, N, d = k.shape
+    _ring_shape_check(q, k, v, P, query_blocks)
+    for name, t in (("out", out), ("dout", dout)):
+        if t.shape != q.shape:
+            raise ValueError(f"{name} must have q's shape")
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != tuple(q.shape[:3]):
+        raise ValueError("lse must be a contiguous float32 [B, H, rows] tensor")
+    if not (q.dtype == k.dtype == v.dtype == out.dtype == dout.dtype):
+        raise TypeError("q, k, v, out and dout must have one dtype")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if dq.shape != q.shape or dk.shape != k.shape or dv.shape != v.shape:
+        raise ValueError("dq, dk, dv must have the shapes of q, k, v")
+    n_q = P if query_blocks is None else len(query_blocks)
+    qb = None if query_blocks is None else (ctypes.c_int32 * max(1, n_q))(*[int(x) for x in query_blocks])
+    ws_ptr, ws_bytes = ctypes.c_void_p(None), 0
+    if workspace is not None:
+        ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+    _check(load().ra_ring_backward(
+        _dev(q, "q"), _strides(q), _dev(k, "k"), _strides(k), _dev(v, "v"), _strides(v), _dev(out, "out"),
+        _strides(out), _dev(dout, "dout"), _strides(dout), _dev(lse, "lse"), _dev(dq, "dq"), _strides(dq),
+        _dev(dk, "dk"), _strides(dk), _dev(dv, "dv"), _strides(dv), _dtype_code(q), B, H, N, d, int(P), qb, n_q,
+        float(scale), _layout_code(layout), ws_ptr, ws_bytes, _stream(stream)))
+    return dq, dk, dv
+
+
+def _ring_shape_check(q, k, v, P, query_blocks):
+    B, H, N, d = k.shape
     if v.shape != k.shape:
         raise ValueError("k and v must have the same shape")
-    n_q = P if query_blocks is None else len(query_blocks)
     if 1 <= P <= N:
         sizes = block_sizes(N, P)
         qb = range(P) if query_blocks is None else query_blocks
@@ -272,6 +338,14 @@ def _ring(q, k, v, P, query_blocks, out, scale, workspace, stream, layout):
         if q.shape[:2] != k.shape[:2] or q.shape[3] != d or q.shape[2] != rows:
             raise ValueError(f"q must be [B, H, rows of the resident blocks, d] = [{B}, {H}, {rows}, {d}], "
                              f"got {tuple(q.shape)}")
+
+
+def _ring(q, k, v, P, query_blocks, out, scale, workspace, stream, layout, lse=None):
+    import torch
+
+    B, H, N, d = k.shape
+    _ring_shape_check(q, k, v, P, query_blocks)
+    n_q = P if query_blocks is None else len(query_blocks)
     if out is not None and out.shape != q.shape:
         raise ValueError("out must have q's shape")
     if out is None:
@@ -286,7 +360,10 @@ def _ring(q, k, v, P, query_blocks, out, scale, workspace, stream, layout):
         raise TypeError("q, k, v and out must have one dtype")
     args = (_dev(q, "q"), _strides(q), _dev(k, "k"), _strides(k), _dev(v, "v"), _strides(v), _dev(out, "out"),
             _strides(out), _dtype_code(q), B, H, N, d, int(P), qb, n_q, float(scale))
-    if layout is None:
+    if lse is not None:
+        _check(load().ra_ring_forward_ex(*args[:8], _dev(lse, "lse"), *args[8:], _layout_code(layout), ws_ptr,
+                                         ws_bytes, _stream(stream)))
+    elif layout is None:
         _check(load().ra_ring_forward(*args, ws_ptr, ws_bytes, _stream(stream)))
     else:
         _check(load().ra_ring_forward_causal(*args, _layout_code(layout), ws_ptr, ws_bytes, _stream(stream)))

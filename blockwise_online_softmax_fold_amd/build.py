@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libra.so")
-SOURCES = ["ra_api.hip", "fold_bf16.hip", "fold_f32.hip", "state.hip"]
+SOURCES = ["ra_api.hip", "fold_bf16.hip", "fold_f32.hip", "fold_bwd_bf16.hip", "fold_bwd_f32.hip", "state.hip"]
 ARCH = "gfx950"
 
 

@@ -160,6 +160,7 @@ __global__ __launch_bounds__(256) void fold_f32_kernel(const FoldParams p) {
   if (!row_ok) return;
   if (p.flags & kWriteOut) {
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    if (p.lse != nullptr && sub == 0) p.lse[st_row] = l > 0.0f ? (mc + log2f(l)) * kLn2 : -INFINITY;
     float* op = (float*)p.out + bi * p.out_sb + hi * p.out_sh + srow * p.out_sr + col0;
 #pragma unroll
     for (int c = 0; c < 16; ++c) {

@@ -45,6 +45,7 @@ struct FoldParams {
   int32_t q_rows;
   int32_t flags;
   float scale_log2;  // softmax scale times log2(e): scores are exponentiated in base 2
+  float* lse;        // with kWriteOut, if not null: m + ln l of each row (the state row layout)
   // Causal masking (mask != kMaskNone): query row r of resident r_ and key row c
   // of its visiting block sit at sequence positions pos(q_blk[r_], r) and
   // pos(kv_blk[r_], c) of a P-device ring over N = P blk + rem tokens (device
@@ -102,10 +103,64 @@ __host__ __device__ inline int32_t last_key_at_or_before(int mode, int32_t P, in
   return c < n - 1 ? c : n - 1;
 }
 
+// One backward launch over n_res (resident query block, visiting block) pairs
+// of one ring step.  The dQ pass (one workgroup per 128 query rows) folds the
+// visiting block into dQ; the dK/dV pass (one workgroup per 128 keys) adds the
+// resident block's share to the visiting block's dK, dV accumulators.  Row
+// arrays (nl2, dd, dq_acc) follow the resident rows like the forward state;
+// dk_acc, dv_acc are [B, H, N, d] over the whole sequence.
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  void* dq;
+  int64_t q_sb, q_sh, q_sr;
+  int64_t k_sb, k_sh, k_sr;
+  int64_t v_sb, v_sh, v_sr;
+  int64_t do_sb, do_sh, do_sr;
+  int64_t dq_sb, dq_sh, dq_sr;
+  const float* nl2;  // -(m + ln l) log2(e) of each query row; -inf for a row that saw no key
+  const float* dd;   // rowsum(dO * O) of each query row
+  float* dq_acc;     // dQ / scale so far, fp32
+  float* dk_acc;     // dK / scale so far, fp32
+  float* dv_acc;     // dV so far, fp32
+  int64_t st_bh;     // rows per (batch, head) of nl2, dd, dq_acc
+  int64_t acc_bh;    // rows per (batch, head) of dk_acc, dv_acc
+  int64_t k_off[kMaxResident];
+  int64_t v_off[kMaxResident];
+  int64_t acc_row0[kMaxResident];  // first row of the visiting block in dk_acc / dv_acc
+  int64_t q_row0[kMaxResident];    // first row of the resident block in q, dout, dq and the row arrays
+  int32_t q_len[kMaxResident];
+  int32_t kv_len[kMaxResident];
+  int32_t q_blk[kMaxResident];
+  int32_t kv_blk[kMaxResident];
+  int32_t B, H, n_res;
+  int32_t q_rows, kv_rows;  // largest q_len and kv_len: they size the grids
+  int32_t flags;            // dQ pass: kLoadState / kStoreState / kWriteOut on dq_acc and dq
+  float scale;
+  float scale_log2;
+  int32_t mask, P, blk, rem;
+};
+
 // Each launcher returns the launch status (hipGetLastError after the launch).
 hipError_t launch_fold_bf16(const FoldParams& p, int d, hipStream_t s);
 hipError_t launch_fold_f32(const FoldParams& p, int d, hipStream_t s);
 hipError_t launch_state_init(float* m, float* l, float* o, int64_t rows_total, int d, hipStream_t s);
+hipError_t launch_bwd_dq_bf16(const BwdParams& p, int d, hipStream_t s);
+hipError_t launch_bwd_dkdv_bf16(const BwdParams& p, int d, hipStream_t s);
+hipError_t launch_bwd_dq_f32(const BwdParams& p, int d, hipStream_t s);
+hipError_t launch_bwd_dkdv_f32(const BwdParams& p, int d, hipStream_t s);
+// Backward set-up per resident row: nl2 = -lse log2(e) (-inf where lse = -inf)
+// and dd = rowsum(dO * O), for B*H*rows rows (row = (bi * H + hi) * rows + r).
+hipError_t launch_bwd_prep(const float* lse, const void* dout, int64_t do_sb, int64_t do_sh, int64_t do_sr,
+                           const void* out, int64_t o_sb, int64_t o_sh, int64_t o_sr, bool bf16, int B, int H,
+                           int64_t rows, int d, float* nl2, float* dd, hipStream_t s);
+// dst = alpha * acc ([B, H, rows, d] fp32, contiguous) in the output dtype with strides.
+hipError_t launch_scale_cast(const float* acc, float alpha, void* dst, int64_t sb, int64_t sh, int64_t sr, bool bf16,
+                             int B, int H, int64_t rows, int d, hipStream_t s);
+// Fill n floats with zero.
+hipError_t launch_zero(float* x, int64_t n, hipStream_t s);
 // out element (bi, hi, row, c) = o / l, 0 where l == 0; out_bf16 selects the output type.
 hipError_t launch_finalize(const float* l, const float* o, void* out, bool out_bf16, int64_t out_sb,
                            int64_t out_sh, int64_t out_sr, int B, int H, int64_t rows, int d, hipStream_t s);

@@ -439,12 +439,13 @@ namespace {
 ra_status_t ring_forward_impl(const void* q, const int64_t q_strides[3], const void* k, const int64_t k_strides[3],
                               const void* v, const int64_t v_strides[3], void* out, const int64_t out_strides[3],
                               ra_dtype_t dt, int64_t B, int64_t H, int64_t N, int64_t d, int32_t P,
-                              const int32_t* query_blocks, int32_t n_q, float scale, int mask, void* workspace,
-                              size_t workspace_bytes, void* stream_) {
+                              const int32_t* query_blocks, int32_t n_q, float scale, int mask, float* lse,
+                              void* workspace, size_t workspace_bytes, void* stream_) {
   ra_status_t st = check_ring(q, q_strides, k, k_strides, v, v_strides, out, out_strides, dt, B, H, N, d, P,
                               query_blocks, n_q);
   if (st != RA_OK) return st;
   if ((st = check_causal(mask, P, N)) != RA_OK) return st;
+  if (lse != nullptr && ((uintptr_t)lse & 3) != 0) return fail(RA_E_INVALID_ARG, "lse is not 4-byte aligned");
   float sc;
   if ((st = resolve_scale(scale, d, &sc)) != RA_OK) return st;
   const RingLayout L = ring_layout(dt, B, H, N, d, P, n_q);
@@ -544,6 +545,7 @@ ra_status_t ring_forward_impl(const void* q, const int64_t q_strides[3], const v
       p.P = P;
       p.blk = (int32_t)bk.b;
       p.rem = (int32_t)bk.rem;
+      p.lse = lse == nullptr ? nullptr : lse + row_of[r0];
       p.q_rows = 0;
       for (int32_t r = 0; r < nr; ++r) {
         const int32_t i = qb(r0 + r);
@@ -579,7 +581,7 @@ RA_API ra_status_t ra_ring_forward(const void* q, const int64_t q_strides[3], co
                                    void* workspace, size_t workspace_bytes, void* stream) {
   g_err.clear();
   return ring_forward_impl(q, q_strides, k, k_strides, v, v_strides, out, out_strides, dt, B, H, N, d, P,
-                           query_blocks, n_q, scale, ra::kMaskNone, workspace, workspace_bytes, stream);
+                           query_blocks, n_q, scale, ra::kMaskNone, nullptr, workspace, workspace_bytes, stream);
 }
 
 RA_API ra_status_t ra_ring_forward_causal(const void* q, const int64_t q_strides[3], const void* k,
@@ -591,7 +593,175 @@ RA_API ra_status_t ra_ring_forward_causal(const void* q, const int64_t q_strides
   g_err.clear();
   if (!valid_layout((int)layout)) return fail(RA_E_INVALID_ARG, "unknown causal layout %d", (int)layout);
   return ring_forward_impl(q, q_strides, k, k_strides, v, v_strides, out, out_strides, dt, B, H, N, d, P,
-                           query_blocks, n_q, scale, (int)layout, workspace, workspace_bytes, stream);
+                           query_blocks, n_q, scale, (int)layout, nullptr, workspace, workspace_bytes, stream);
+}
+
+RA_API ra_status_t ra_ring_forward_ex(const void* q, const int64_t q_strides[3], const void* k,
+                                      const int64_t k_strides[3], const void* v, const int64_t v_strides[3], void* out,
+                                      const int64_t out_strides[3], float* lse, ra_dtype_t dt, int64_t B, int64_t H,
+                                      int64_t N, int64_t d, int32_t P, const int32_t* query_blocks, int32_t n_q,
+                                      float scale, ra_causal_t layout, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  g_err.clear();
+  if (!valid_layout((int)layout)) return fail(RA_E_INVALID_ARG, "unknown causal layout %d", (int)layout);
+  return ring_forward_impl(q, q_strides, k, k_strides, v, v_strides, out, out_strides, dt, B, H, N, d, P,
+                           query_blocks, n_q, scale, (int)layout, lse, workspace, workspace_bytes, stream);
+}
+
+namespace {
+
+// Workspace of the ring backward: per resident row nl2 and dd, the fp32 dQ
+// accumulator, then fp32 dK and dV accumulators over the whole sequence.
+struct BwdLayout {
+  Blocks blk;
+  size_t off_nl2 = 0, off_dd = 0, off_dq = 0, off_dk = 0, off_dv = 0, total = 0;
+};
+
+BwdLayout bwd_layout(int64_t B, int64_t H, int64_t N, int64_t d, int32_t P, int32_t n_q) {
+  BwdLayout L;
+  L.blk = ring_blocks(N, P);
+  const size_t rows = (size_t)B * H * n_q * L.blk.b_max;
+  const size_t seq = (size_t)B * H * N;
+  L.off_nl2 = 0;
+  L.off_dd = round_up(L.off_nl2 + rows * 4);
+  L.off_dq = round_up(L.off_dd + rows * 4);
+  L.off_dk = round_up(L.off_dq + rows * (size_t)d * 4);
+  L.off_dv = round_up(L.off_dk + seq * (size_t)d * 4);
+  L.total = round_up(L.off_dv + seq * (size_t)d * 4);
+  return L;
+}
+
+hipError_t launch_bwd(const ra::BwdParams& p, ra_dtype_t dt, int d, hipStream_t s) {
+  hipError_t e = dt == RA_DTYPE_BF16 ? ra::launch_bwd_dq_bf16(p, d, s) : ra::launch_bwd_dq_f32(p, d, s);
+  if (e != hipSuccess) return e;
+  return dt == RA_DTYPE_BF16 ? ra::launch_bwd_dkdv_bf16(p, d, s) : ra::launch_bwd_dkdv_f32(p, d, s);
+}
+
+}  // namespace
+
+RA_API size_t ra_ring_backward_workspace_bytes(ra_dtype_t dt, int64_t B, int64_t H, int64_t N, int64_t d, int32_t P,
+                                               int32_t n_q) {
+  const std::string saved = g_err;
+  const bool ok = check_common(dt, B, H, d) == RA_OK && P >= 1 && N >= P && n_q >= 1 &&
+                  N / P + 1 <= 0x7fffffffLL / 4;
+  g_err = saved;
+  if (!ok) return 0;
+  return bwd_layout(B, H, N, d, P, n_q).total;
+}
+
+RA_API ra_status_t ra_ring_backward(const void* q, const int64_t q_strides[3], const void* k,
+                                    const int64_t k_strides[3], const void* v, const int64_t v_strides[3],
+                                    const void* out, const int64_t out_strides[3], const void* dout,
+                                    const int64_t dout_strides[3], const float* lse, void* dq,
+                                    const int64_t dq_strides[3], void* dk, const int64_t dk_strides[3], void* dv,
+                                    const int64_t dv_strides[3], ra_dtype_t dt, int64_t B, int64_t H, int64_t N,
+                                    int64_t d, int32_t P, const int32_t* query_blocks, int32_t n_q, float scale,
+                                    ra_causal_t layout, void* workspace, size_t workspace_bytes, void* stream_) {
+  g_err.clear();
+  ra_status_t st = check_ring(q, q_strides, k, k_strides, v, v_strides, out, out_strides, dt, B, H, N, d, P,
+                              query_blocks, n_q);
+  if (st != RA_OK) return st;
+  if (!valid_layout((int)layout)) return fail(RA_E_INVALID_ARG, "unknown causal layout %d", (int)layout);
+  if ((st = check_causal((int)layout, P, N)) != RA_OK) return st;
+  if ((st = check_tensor("dout", dout, dout_strides, dt)) != RA_OK) return st;
+  if ((st = check_tensor("dq", dq, dq_strides, dt)) != RA_OK) return st;
+  if ((st = check_tensor("dk", dk, dk_strides, dt)) != RA_OK) return st;
+  if ((st = check_tensor("dv", dv, dv_strides, dt)) != RA_OK) return st;
+  if (lse == nullptr) return fail(RA_E_INVALID_ARG, "lse is NULL");
+  if (((uintptr_t)lse & 3) != 0) return fail(RA_E_INVALID_ARG, "lse is not 4-byte aligned");
+  float sc;
+  if ((st = resolve_scale(scale, d, &sc)) != RA_OK) return st;
+  const BwdLayout L = bwd_layout(B, H, N, d, P, n_q);
+  if (workspace != nullptr) {
+    if (workspace_bytes < L.total)
+      return fail(RA_E_INVALID_ARG, "workspace of %zu bytes is smaller than the %zu bytes needed", workspace_bytes,
+                  L.total);
+    if (((uintptr_t)workspace & (kAlign - 1)) != 0)
+      return fail(RA_E_INVALID_ARG, "workspace is not %zu-byte aligned", kAlign);
+  }
+  auto qb = [&](int32_t r) { return query_blocks ? query_blocks[r] : r; };
+  const Blocks& bk = L.blk;
+  std::vector<int64_t> row_of(n_q + 1, 0);
+  for (int32_t r = 0; r < n_q; ++r) row_of[r + 1] = row_of[r] + bk.len(qb(r));
+  const int64_t rows = row_of[n_q];
+  hipStream_t stream = (hipStream_t)stream_;
+  const size_t es = esize(dt);
+  const bool bf16 = dt == RA_DTYPE_BF16;
+
+  void* ws = workspace;
+  const bool own_ws = ws == nullptr;
+  if (own_ws) RA_HIP(hipMallocAsync(&ws, L.total, stream), "hipMallocAsync (backward workspace)");
+  char* base = (char*)ws;
+  float* nl2 = (float*)(base + L.off_nl2);
+  float* dd = (float*)(base + L.off_dd);
+  float* dq_acc = (float*)(base + L.off_dq);
+  float* dk_acc = (float*)(base + L.off_dk);
+  float* dv_acc = (float*)(base + L.off_dv);
+
+  RA_HIP(ra::launch_bwd_prep(lse, dout, dout_strides[0], dout_strides[1], dout_strides[2], out, out_strides[0],
+                             out_strides[1], out_strides[2], bf16, (int)B, (int)H, rows, (int)d, nl2, dd, stream),
+         "backward set-up launch");
+  RA_HIP(ra::launch_zero(dk_acc, B * H * N * d, stream), "zero launch");
+  RA_HIP(ra::launch_zero(dv_acc, B * H * N * d, stream), "zero launch");
+
+  for (int t = 0; t < P; ++t) {
+    for (int32_t r0 = 0; r0 < n_q; r0 += ra::kMaxResident) {
+      const int32_t nr = n_q - r0 < ra::kMaxResident ? n_q - r0 : ra::kMaxResident;
+      ra::BwdParams p = {};
+      p.q = (const char*)q + (size_t)row_of[r0] * q_strides[2] * es;
+      p.dout = (const char*)dout + (size_t)row_of[r0] * dout_strides[2] * es;
+      p.dq = (char*)dq + (size_t)row_of[r0] * dq_strides[2] * es;
+      p.k = k;
+      p.v = v;
+      set_strides(&p.q_sb, &p.q_sh, &p.q_sr, q_strides);
+      set_strides(&p.k_sb, &p.k_sh, &p.k_sr, k_strides);
+      set_strides(&p.v_sb, &p.v_sh, &p.v_sr, v_strides);
+      set_strides(&p.do_sb, &p.do_sh, &p.do_sr, dout_strides);
+      set_strides(&p.dq_sb, &p.dq_sh, &p.dq_sr, dq_strides);
+      p.nl2 = nl2 + row_of[r0];
+      p.dd = dd + row_of[r0];
+      p.dq_acc = dq_acc + (size_t)row_of[r0] * d;
+      p.dk_acc = dk_acc;
+      p.dv_acc = dv_acc;
+      p.st_bh = rows;
+      p.acc_bh = N;
+      p.B = (int32_t)B;
+      p.H = (int32_t)H;
+      p.n_res = nr;
+      p.flags = (t == 0 ? 0 : ra::kLoadState) | (t == P - 1 ? ra::kWriteOut : ra::kStoreState);
+      p.scale = sc;
+      p.scale_log2 = to_log2_scale(sc);
+      p.mask = (int)layout;
+      p.P = P;
+      p.blk = (int32_t)bk.b;
+      p.rem = (int32_t)bk.rem;
+      p.q_rows = 0;
+      p.kv_rows = 0;
+      for (int32_t r = 0; r < nr; ++r) {
+        const int32_t i = qb(r0 + r);
+        const int32_t j = (int32_t)(((int64_t)i - t) % P + P) % P;
+        p.q_blk[r] = i;
+        p.kv_blk[r] = j;
+        p.q_len[r] = (int32_t)bk.len(i);
+        p.kv_len[r] = (int32_t)bk.len(j);
+        p.q_row0[r] = row_of[r0 + r] - row_of[r0];
+        p.k_off[r] = bk.start(j) * k_strides[2];
+        p.v_off[r] = bk.start(j) * v_strides[2];
+        p.acc_row0[r] = bk.start(j);
+        if (p.q_len[r] > p.q_rows) p.q_rows = p.q_len[r];
+        if (p.kv_len[r] > p.kv_rows) p.kv_rows = p.kv_len[r];
+      }
+      RA_HIP(launch_bwd(p, dt, (int)d, stream), "backward launch");
+    }
+  }
+  RA_HIP(ra::launch_scale_cast(dk_acc, sc, dk, dk_strides[0], dk_strides[1], dk_strides[2], bf16, (int)B, (int)H, N,
+                               (int)d, stream),
+         "dK cast launch");
+  RA_HIP(ra::launch_scale_cast(dv_acc, 1.0f, dv, dv_strides[0], dv_strides[1], dv_strides[2], bf16, (int)B, (int)H, N,
+                               (int)d, stream),
+         "dV cast launch");
+  if (own_ws) RA_HIP(hipFreeAsync(ws, stream), "hipFreeAsync (backward workspace)");
+  return RA_OK;
 }
 
 RA_API ra_status_t ra_profile_folds(int enable) {

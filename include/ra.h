@@ -208,6 +208,56 @@ ra_status_t ra_ring_forward_causal(const void* q, const int64_t q_strides[3], co
                                    ra_causal_t layout, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * ra_ring_forward_ex -- ra_ring_forward_causal (RA_CAUSAL_NONE: ra_ring_forward)
+ * that also writes, when lse is not NULL, each resident row's log-sum-exp
+ * L = m + ln l (natural log, the scaled scores' units) into lse: float32
+ * [B, H, rows] contiguous, rows stacked like q; -inf for a row that saw no
+ * key.  The backward pass needs L to rebuild the attention weights.
+ */
+ra_status_t ra_ring_forward_ex(const void* q, const int64_t q_strides[3], const void* k, const int64_t k_strides[3],
+                               const void* v, const int64_t v_strides[3], void* out, const int64_t out_strides[3],
+                               float* lse, ra_dtype_t dt, int64_t B, int64_t H, int64_t N, int64_t d, int32_t P,
+                               const int32_t* query_blocks, int32_t n_q, float scale, ra_causal_t layout,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ra_ring_backward_workspace_bytes -- device workspace ra_ring_backward needs:
+ * per resident row two floats and a float32 dQ row, plus float32 dK and dV
+ * accumulators over the whole sequence ([B, H, N, d] each).  Returns 0 for
+ * arguments ra_ring_backward would reject.
+ */
+size_t ra_ring_backward_workspace_bytes(ra_dtype_t dt, int64_t B, int64_t H, int64_t N, int64_t d, int32_t P,
+                                        int32_t n_q);
+
+/*
+ * ra_ring_backward -- the backward pass on the same ring (vibeengines.com "Ring
+ * attention, explained", method step 6): on step t resident block i folds
+ * block j = (i - t) mod P, adding to its own dQ_i and to the visiting block's
+ * dK_j, dV_j accumulators (which, on a real ring, travel with the block).
+ * With P = softmax weights rebuilt from lse: dV = P^T dO, dP = dO V^T,
+ * D = rowsum(dO * O), dS = P * (dP - D), dQ = scale dS K, dK = scale dS^T Q.
+ *
+ * q, k, v, layout, query_blocks, n_q, scale: exactly as given to the forward.
+ * out, lse: the forward's output and log-sum-exp (ra_ring_forward_ex).
+ * dout: dL/dO, like out.  dq: like q, receives dL/dQ of the resident rows.
+ * dk, dv: [B, H, N, d] like k and v, overwritten with the resident blocks'
+ *      shares of dL/dK and dL/dV (the full gradients when every block is
+ *      resident).  All of dtype dt; strides in elements.
+ * Accumulation is in float32; bf16 inputs use bf16 MFMA products with the
+ * weights and dS rounded to bf16.  K and V are read in place (one GPU: the
+ * blocks do not move).  workspace: at least ra_ring_backward_workspace_bytes
+ * bytes, 256-byte aligned, or NULL for a stream-ordered internal one.
+ */
+ra_status_t ra_ring_backward(const void* q, const int64_t q_strides[3], const void* k, const int64_t k_strides[3],
+                             const void* v, const int64_t v_strides[3], const void* out,
+                             const int64_t out_strides[3], const void* dout, const int64_t dout_strides[3],
+                             const float* lse, void* dq, const int64_t dq_strides[3], void* dk,
+                             const int64_t dk_strides[3], void* dv, const int64_t dv_strides[3], ra_dtype_t dt,
+                             int64_t B, int64_t H, int64_t N, int64_t d, int32_t P, const int32_t* query_blocks,
+                             int32_t n_q, float scale, ra_causal_t layout, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/*
  * Measurement support (not part of the method).  While enabled on the calling
  * process, ra_ring_forward records a HIP event pair around every fold launch,
  * on the caller's stream that the launch uses.  ra_profile_read waits for the

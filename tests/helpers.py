@@ -68,3 +68,25 @@ def oracle_rows(q, k, v, rows: np.ndarray, heads=None, scale=None) -> np.ndarray
 
 def default_scale(d: int) -> float:
     return 1.0 / math.sqrt(d)
+
+
+def check_grad(got, ref: np.ndarray, dtype: str, what: str = "") -> dict:
+    """Gradient parity, norm-wise: the output bars scaled by the gradient's own
+    magnitude (a gradient has no fixed scale, unlike O, a convex combination of
+    V rows): bf16 max|err| <= 2e-2 max|ref| and mean|err| <= 2e-3 max|ref|;
+    fp32 max|err| <= 1e-5 max|ref|."""
+    g = to64(got) if not isinstance(got, np.ndarray) else got
+    assert g.shape == ref.shape, (g.shape, ref.shape)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite gradient"
+    err = np.abs(g - ref)
+    scale = float(np.abs(ref).max())
+    figs = dict(max_abs=float(err.max()), mean_abs=float(err.mean()), ref_max=scale)
+    if scale == 0.0:
+        assert figs["max_abs"] == 0.0, f"{what}: expected zeros"
+        return figs
+    if dtype == "bf16":
+        assert figs["max_abs"] <= BF16_MAX_ABS * scale, f"{what}: max-abs {figs['max_abs']:.3g} > 2e-2 * {scale:.3g}"
+        assert figs["mean_abs"] <= BF16_MEAN_ABS * scale, f"{what}: mean-abs {figs['mean_abs']:.3g} > 2e-3 * {scale:.3g}"
+    else:
+        assert figs["max_abs"] <= F32_REL * scale, f"{what}: max-abs {figs['max_abs']:.3g} > 1e-5 * {scale:.3g}"
+    return figs

@@ -195,3 +195,39 @@ def _ring_causal(lib, layout=1, N=131072, P=16, n_q=16, d=128):
 def test_ring_forward_causal_rejects(lib, kwargs, status, needle):
     assert _ring_causal(lib, **kwargs) == status
     assert needle in lib.ra_last_error().decode()
+
+
+def _bwd(lib, lse=A, dout=A, layout=0, N=4096, P=4, ws=None, ws_bytes=0, d=128):
+    S = S_BF16
+    return lib.ra_ring_backward(A, S, A, S, A, S, A, S, dout, S, lse, A, S, A, S, A, S, BF16, 1, 16, N, d, P, None,
+                                P, ctypes.c_float(0.0), layout, ws if ws is not None else ctypes.c_void_p(None),
+                                ws_bytes, None)
+
+
+@pytest.mark.parametrize("kwargs,status,needle", [
+    (dict(lse=ctypes.c_void_p(None)), 1, "lse is NULL"),
+    (dict(lse=ctypes.c_void_p(0x10002)), 1, "lse is not 4-byte aligned"),
+    (dict(dout=ctypes.c_void_p(None)), 1, "dout is NULL"),
+    (dict(layout=7), 1, "unknown causal layout"),
+    (dict(layout=3, N=4100), 1, "multiple of 2P"),
+    (dict(d=96), 2, "head dim"),
+    (dict(ws=ctypes.c_void_p(0x10000), ws_bytes=4096), 1, "smaller than"),
+])
+def test_ring_backward_rejects(lib, kwargs, status, needle):
+    assert _bwd(lib, **kwargs) == status
+    assert needle in lib.ra_last_error().decode()
+
+
+def test_ring_backward_workspace_size(lib):
+    B, H, N, d, P = 1, 2, 1000, 64, 3
+    got = lib.ra_ring_backward_workspace_bytes(BF16, B, H, N, d, P, P)
+    rows = P * (N // P + 1)
+    need = 2 * B * H * rows * 4 + B * H * rows * d * 4 + 2 * B * H * N * d * 4
+    assert need <= got <= need + 5 * 256
+    assert lib.ra_ring_backward_workspace_bytes(BF16, B, H, 2, d, 3, 3) == 0  # N < P
+
+
+def test_ring_forward_ex_rejects_misaligned_lse(lib):
+    st = lib.ra_ring_forward_ex(A, S_BF16, A, S_BF16, A, S_BF16, A, S_BF16, ctypes.c_void_p(0x10001), BF16, 1, 32,
+                                131072, 128, 16, None, 16, ctypes.c_float(0.0), 0, ctypes.c_void_p(None), 0, None)
+    assert st == 1 and "lse" in lib.ra_last_error().decode()
