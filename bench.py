@@ -7,13 +7,16 @@ query block, including the final normalisation.  Inputs are resident in HBM
 before timing starts.  Prints ONE JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
-                    [--causal contiguous|striped|zigzag]
+                    [--causal contiguous|striped|zigzag] [--backward]
                     [--no-cpu-baseline] [--cpu-seconds S]
 
 The default workload is the 128K-token ring (B1 H32 d128 N131072 P16, all 16
 query blocks resident), non-causal.  With --causal the same inputs are taken
 as dealt to the devices in that token layout and the causal ring runs; its
-TFLOP/s count only the visible (query, key) pairs, 4 d FLOP each.
+TFLOP/s count only the visible (query, key) pairs, 4 d FLOP each.  With
+--backward one step is one ra_ring_backward (dQ, dK, dV on the same ring; the
+forward that gives O and the log-sum-exp runs once, untimed), counted as the
+five products of the backward, 10 d FLOP per (query, key) pair.
 """
 
 from __future__ import annotations
@@ -130,6 +133,7 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--causal", choices=("contiguous", "striped", "zigzag"), default=None,
                     help="run the causal ring with the inputs in this token layout")
+    ap.add_argument("--backward", action="store_true", help="time the ring backward instead of the forward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -160,8 +164,20 @@ def main() -> int:
                      device="cuda")
     qb = w.query_blocks
 
+    if args.backward:
+        out, lse = ra.ra_ring_forward_ex(q, k, v, w.P, args.causal, query_blocks=qb)
+        dout = torch.randn(out.shape, generator=torch.Generator(device="cuda").manual_seed(w.seed + 7),
+                           device="cuda").to(out.dtype)
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+        del ws
+        ws = torch.empty(ra.ra_ring_backward_workspace_bytes(q.dtype, w.B, w.H, w.N, w.d, w.P, w.n_q),
+                         dtype=torch.uint8, device="cuda")
+
     def step():
-        if args.causal:
+        if args.backward:
+            ra.ra_ring_backward(q, k, v, out, dout, lse, w.P, args.causal, query_blocks=qb, dq=grads[0],
+                                dk=grads[1], dv=grads[2], workspace=ws)
+        elif args.causal:
             ra.ra_ring_forward_causal(q, k, v, w.P, args.causal, query_blocks=qb, out=out, workspace=ws)
         else:
             ra.ra_ring_forward(q, k, v, w.P, query_blocks=qb, out=out, workspace=ws)
@@ -192,7 +208,8 @@ def main() -> int:
     ra.ra_profile_folds(False)
     print(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
 
-    flops = w.flops() if not args.causal else 4.0 * w.d * _visible_pairs(w, args.causal)
+    pairs = (w.flops() / (4.0 * w.d)) if not args.causal else _visible_pairs(w, args.causal)
+    flops = (10.0 if args.backward else 4.0) * w.d * pairs
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK[w.dtype]
     launches_per_step = launches / args.steps
@@ -205,15 +222,16 @@ def main() -> int:
         "peak": peak,
         "unit": "TFLOP/s",
         "frac": round(achieved / peak, 4),
-        "traffic": _traffic(w.name, w.dtype),
-        "kernel": f"fold_{w.dtype}_kernel<{w.d}>",
+        "traffic": None if args.backward else _traffic(w.name, w.dtype),
+        "kernel": (f"bwd_dq_kernel<{w.d}> + bwd_dkdv_kernel<{w.d}> (one step)" if args.backward
+                   else f"fold_{w.dtype}_kernel<{w.d}>"),
         "flop_per_launch": flops_per_launch,
         "avg_launch_ms": round(fold_avg_ms, 4),
         "max_launch_ms": round(fold_ms_max, 4),
         "launches": launches,
     }
     rec = {
-        "metric": METRIC,
+        "metric": METRIC if not args.backward else METRIC.replace("ring-fold attention", "ring-fold attention backward"),
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -226,9 +244,10 @@ def main() -> int:
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "P": w.P, "b": w.b,
-                   "resident_query_blocks": w.n_q, "seed": w.seed, "causal": args.causal or False},
+                   "resident_query_blocks": w.n_q, "seed": w.seed, "causal": args.causal or False,
+                   "pass": "backward" if args.backward else "forward"},
         "pct_mfma_peak": round(100.0 * tflops / peak, 2),
-        "exps_per_s": (w.exps() if not args.causal else _visible_pairs(w, args.causal)) / (ms * 1e-3),
+        "exps_per_s": pairs * (2.0 if args.backward else 1.0) / (ms * 1e-3),
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:

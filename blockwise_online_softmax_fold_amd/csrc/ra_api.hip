@@ -751,7 +751,9 @@ RA_API ra_status_t ra_ring_backward(const void* q, const int64_t q_strides[3], c
         if (p.q_len[r] > p.q_rows) p.q_rows = p.q_len[r];
         if (p.kv_len[r] > p.kv_rows) p.kv_rows = p.kv_len[r];
       }
+      const long pi = prof_begin(stream);
       RA_HIP(launch_bwd(p, dt, (int)d, stream), "backward launch");
+      prof_end(pi, stream);
     }
   }
   RA_HIP(ra::launch_scale_cast(dk_acc, sc, dk, dk_strides[0], dk_strides[1], dk_strides[2], bf16, (int)B, (int)H, N,

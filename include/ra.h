@@ -259,8 +259,9 @@ ra_status_t ra_ring_backward(const void* q, const int64_t q_strides[3], const vo
 
 /*
  * Measurement support (not part of the method).  While enabled on the calling
- * process, ra_ring_forward records a HIP event pair around every fold launch,
- * on the caller's stream that the launch uses.  ra_profile_read waits for the
+ * process, the ring drivers record a HIP event pair around every fold launch
+ * (forward) and every step's dQ + dK/dV launch pair (backward), on the
+ * caller's stream that the launches use.  ra_profile_read waits for the
  * recorded events, returns the number of fold launches, their summed and
  * largest durations in milliseconds, and clears the record.  Enabling or
  * disabling also clears it.  At most 4096 launches are recorded; later ones
