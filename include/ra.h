@@ -68,7 +68,7 @@ typedef enum { RA_DTYPE_F32 = 0, RA_DTYPE_BF16 = 1 } ra_dtype_t;
  * block (b = N/P rows when P divides N; see "Blocks of the ring") holds
  * sequence position
  *   RA_CAUSAL_CONTIGUOUS: start_j + r, start_j = j*b + min(j, N mod P)
- *   RA_CAUSAL_STRIPED:    r*P + j                     (round-robin, "striped")
+ *   RA_CAUSAL_STRIPED:    r*P + j                     (tokens handed out in turn)
  *   RA_CAUSAL_ZIGZAG:     j*h + r          for r < h  (h = b/2: chunk j and its
  *                         (2P-1-j)*h + r-h for r >= h  mirror chunk 2P-1-j)
  * RA_CAUSAL_NONE is full (non-causal) attention.  In every layout positions
@@ -147,7 +147,7 @@ ra_status_t ra_finalize(const float* l, const float* o, void* out, const int64_t
  * divides N every block holds b = N/P rows; otherwise (bembew.net
  * "Implementation Considerations": padding or dynamic partitioning) the first
  * N mod P devices hold N/P + 1 rows and the others N/P, so block j starts at
- * row j*(N/P) + min(j, N mod P).  Dealing tokens round-robin (the striped
+ * row j*(N/P) + min(j, N mod P).  Handing tokens out in turn (the striped
  * layout) gives exactly these sizes.
  */
 

@@ -7,9 +7,9 @@ Sources:
   contiguous blocks of b = N/P tokens, device i owns block i.
 * same page, "Causal masking, load balance, and other wrinkles", and
   vibeengines.com "Ring attention, explained", "The causal-mask catch": a query
-  attends only to keys at or before its own position; striped attention deals
-  tokens to hosts round-robin; the zig-zag split gives each host one early
-  chunk and its mirror-image late chunk.
+  attends only to keys at or before its own position; the striped split hands
+  tokens to the devices in turn; the zig-zag split gives each device an early
+  chunk together with the matching chunk counted from the end.
 
 ``positions(layout, P, b)`` returns pos[j, r], the position in the whole
 sequence of row r of device j's shard.  A tensor "in layout order" holds
@@ -19,7 +19,7 @@ When N is not a multiple of P (bembew.net "Ring Attention", "Implementation
 Considerations": padding or dynamic partitioning is needed), the shards are
 uneven: ``block_positions(layout, P, N)`` lists each device's positions.  The
 contiguous split gives the first N mod P devices one token more (the sizes
-``numpy.array_split`` makes); dealing tokens round-robin (striped) gives
+``numpy.array_split`` makes); handing tokens out in turn (striped) gives
 exactly the same sizes.  The zig-zag split needs N to be a multiple of 2P.
 """
 

@@ -5,8 +5,8 @@
 * brute force in pure Python on tiny inputs;
 * the ring over each layout (contiguous, striped, zig-zag) equals the dense
   causal result after undoing the layout permutation;
-* the load-balance facts the pages state: with contiguous blocks roughly half
-  of the compute slots idle, striped and zig-zag splits even it out;
+* the load-balance facts the pages state: a contiguous split leaves about half
+  of the compute slots unused, striped and zig-zag splits even it out;
 * a block a row cannot see leaves that row's state as it was.
 """
 
@@ -94,7 +94,7 @@ def _work_per_device(layout, P, b):
 
 def test_contiguous_causal_leaves_about_half_idle():
     """Math page, causal section, and vibeengines.com: with contiguous blocks
-    and a lockstep ring, roughly half of all compute slots sit idle; striped
+    and a lockstep ring, about half of the compute slots do nothing; striped
     and zig-zag splits balance the work."""
     P, b = 8, 16
     w = _work_per_device("contiguous", P, b)
