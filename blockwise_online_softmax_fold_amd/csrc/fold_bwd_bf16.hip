@@ -16,13 +16,16 @@
 //    accumulator layout and is directly the B operand of dQ^T += K^T dS^T,
 //    with the K^T operand read from row-major K by ds_read_b64_tr_b16.
 //  * bwd_dkdv_kernel: the transpose of the same pattern -- each wave owns 32
-//    keys (K and V in registers as B operands) and streams the resident
-//    block's Q and dO rows (plus their L and D) through LDS in 32-row tiles;
+//    keys (K in registers, the workgroup's V rows in LDS, both as B operands)
+//    and streams the resident block's Q and dO rows (plus their L and D)
+//    through LDS in 32-row tiles;
 //    S = Q K^T and dP = dO V^T put one key in each lane, and
 //    dV^T += dO^T P, dK^T += Q^T dS read dO^T and Q^T by transposed LDS
 //    reads.  The dK, dV accumulators (fp32, unscaled by s) are loaded and
 //    stored once per launch; one workgroup owns each 128-key tile, so no two
-//    workgroups touch the same rows.
+//    workgroups touch the same rows.  Keeping V in LDS rather than registers
+//    leaves the d <= 128 kernel within 256 VGPRs: two waves per SIMD, and the
+//    MFMA accumulators stay in VGPRs where the VALU reads them directly.
 // Causal masking uses the same prefix argument as the forward: the keys a
 // query sees are a prefix of the visiting block, so the queries a key is seen
 // by are a suffix of the resident block; tiles outside are skipped.
@@ -294,7 +297,7 @@ void bwd_dq_kernel(const BwdParams p) {
 // ---------------------------------------------------------------------------
 // dK, dV: one workgroup per 128 keys of one visiting block.
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1 : 2)))
 void bwd_dkdv_kernel(const BwdParams p) {
   constexpr int TQ = 32;
   constexpr int NC = D / 16;
@@ -305,6 +308,8 @@ void bwd_dkdv_kernel(const BwdParams p) {
   static_assert(CPW >= 1 && TE % 2048 == 0, "tile must split into whole 1 KB chunks per wave");
   __shared__ __attribute__((aligned(1024))) __bf16 lds[2 * 2 * TE];  // [buffer][Q | dO][TQ][D]
   __shared__ __attribute__((aligned(16))) float lrow[2][2 * TQ];     // [buffer][nl2 of TQ rows | dd of TQ rows]
+  constexpr int CPW_V = KT * D / 512 / 4;
+  __shared__ __attribute__((aligned(1024))) __bf16 vlds[KT * D];     // V rows of the workgroup's keys
 
   const int tiles_k = (p.kv_rows + KT - 1) / KT;
   const int total = tiles_k * p.n_res * p.H * p.B;
@@ -340,15 +345,11 @@ void bwd_dkdv_kernel(const BwdParams p) {
     if (q_from >= q_len) return;  // no query of this block sees these keys
   }
 
-  bf16x8 kf[NC], vf[NC];
+  bf16x8 kf[NC];
   {
     const __bf16* kp = (const __bf16*)p.k + bi * p.k_sb + hi * p.k_sh + p.k_off[r] + (int64_t)ck * p.k_sr + 8 * lg;
-    const __bf16* vp = (const __bf16*)p.v + bi * p.v_sb + hi * p.v_sh + p.v_off[r] + (int64_t)ck * p.v_sr + 8 * lg;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      kf[c] = *(const bf16x8*)(kp + 16 * c);
-      vf[c] = *(const bf16x8*)(vp + 16 * c);
-    }
+    for (int c = 0; c < NC; ++c) kf[c] = *(const bf16x8*)(kp + 16 * c);
   }
 
   // dK^T / s and dV^T of this wave's 32 keys: lane (key, half) holds d
@@ -416,7 +417,8 @@ void bwd_dkdv_kernel(const BwdParams p) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(ql + row_rd[c]), kf[c], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(dl + row_rd[c]), vf[c], dp, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(dl + row_rd[c]),
+                                                   *(const bf16x8*)(vlds + wave * 32 * D + row_rd[c]), dp, 0, 0, 0);
     }
     if (masked) {
       const int rbase_t = qt * TQ + 4 * lg;
@@ -458,6 +460,12 @@ void bwd_dkdv_kernel(const BwdParams p) {
   };
 
   if (qt0 < n_qt) {
+    {  // the workgroup's V rows, swizzled like the tiles; they land with the first tile
+      const __bf16* vb = (const __bf16*)p.v + bi * p.v_sb + hi * p.v_sh + p.v_off[r];
+      int ld_voff[CPW_V];
+      tile_offsets<D, CPW_V>(wave, lane, (int)p.v_sr, ld_voff);
+      issue_rows<D, CPW_V, KT>(vb, (int)p.v_sr, ld_voff, kt * KT, kv_len, vlds, wave, lane);
+    }
     issue_tile(qt0, qt0 & 1);
     for (int qt = qt0; qt < n_qt; ++qt) tile(qt, qt & 1, qt < qt_plain || qt >= n_full);
   }
