@@ -308,7 +308,6 @@ void bwd_dkdv_kernel(const BwdParams p) {
   static_assert(CPW >= 1 && TE % 2048 == 0, "tile must split into whole 1 KB chunks per wave");
   __shared__ __attribute__((aligned(1024))) __bf16 lds[2 * 2 * TE];  // [buffer][Q | dO][TQ][D]
   __shared__ __attribute__((aligned(16))) float lrow[2][2 * TQ];     // [buffer][nl2 of TQ rows | dd of TQ rows]
-  constexpr int CPW_V = KT * D / 512 / 4;
   __shared__ __attribute__((aligned(1024))) __bf16 vlds[KT * D];     // V rows of the workgroup's keys
 
   const int tiles_k = (p.kv_rows + KT - 1) / KT;
@@ -460,11 +459,16 @@ void bwd_dkdv_kernel(const BwdParams p) {
   };
 
   if (qt0 < n_qt) {
-    {  // the workgroup's V rows, swizzled like the tiles; they land with the first tile
+    {  // the workgroup's V rows, swizzled like the tiles, in 32-row pieces (so the
+       // byte offsets from each piece's first row stay below 2^31); they land
+       // with the first tile
       const __bf16* vb = (const __bf16*)p.v + bi * p.v_sb + hi * p.v_sh + p.v_off[r];
-      int ld_voff[CPW_V];
-      tile_offsets<D, CPW_V>(wave, lane, (int)p.v_sr, ld_voff);
-      issue_rows<D, CPW_V, KT>(vb, (int)p.v_sr, ld_voff, kt * KT, kv_len, vlds, wave, lane);
+      const int v_sr = (int)p.v_sr;
+      int ld_voff[CPW];
+      tile_offsets<D, CPW>(wave, lane, v_sr, ld_voff);
+#pragma unroll
+      for (int i = 0; i < KT / TQ; ++i)
+        issue_rows<D, CPW, TQ>(vb, v_sr, ld_voff, kt * KT + i * TQ, kv_len, vlds + i * TE, wave, lane);
     }
     issue_tile(qt0, qt0 & 1);
     for (int qt = qt0; qt < n_qt; ++qt) tile(qt, qt & 1, qt < qt_plain || qt >= n_full);

@@ -64,10 +64,13 @@ ra_status_t check_tensor(const char* name, const void* ptr, const int64_t* strid
   return RA_OK;
 }
 
-// The fold kernels address one K/V tile with 32-bit row offsets.
-constexpr int64_t kMaxKvRowStride = (int64_t)1 << 24;
-ra_status_t check_kv_row_stride(const char* name, const int64_t* strides) {
-  if (strides[2] >= kMaxKvRowStride)
+// The kernels address the rows of one LDS tile (at most 64 rows) with 32-bit
+// byte offsets from the tile's first row: streamed operands (K, V in the
+// forward and the dQ kernel, Q, dO and V in the dK/dV kernel) need row strides
+// below 2^24 elements.
+constexpr int64_t kMaxTileRowStride = (int64_t)1 << 24;
+ra_status_t check_tile_row_stride(const char* name, const int64_t* strides) {
+  if (strides[2] >= kMaxTileRowStride)
     return fail(RA_E_UNSUPPORTED, "%s row stride %lld is not below 2^24 elements", name, (long long)strides[2]);
   return RA_OK;
 }
@@ -203,8 +206,8 @@ ra_status_t check_ring(const void* q, const int64_t* q_strides, const void* k, c
   if ((st = check_tensor("k", k, k_strides, dt)) != RA_OK) return st;
   if ((st = check_tensor("v", v, v_strides, dt)) != RA_OK) return st;
   if ((st = check_tensor("out", out, out_strides, dt)) != RA_OK) return st;
-  if ((st = check_kv_row_stride("k", k_strides)) != RA_OK) return st;
-  if ((st = check_kv_row_stride("v", v_strides)) != RA_OK) return st;
+  if ((st = check_tile_row_stride("k", k_strides)) != RA_OK) return st;
+  if ((st = check_tile_row_stride("v", v_strides)) != RA_OK) return st;
   return RA_OK;
 }
 
@@ -324,8 +327,8 @@ ra_status_t fold_block_impl(const void* q, const int64_t q_strides[3], const voi
   if (kv_rows == 0) return RA_OK;  // an empty block leaves the state as it is
   if ((st = check_tensor("k", k, k_strides, dt)) != RA_OK) return st;
   if ((st = check_tensor("v", v, v_strides, dt)) != RA_OK) return st;
-  if ((st = check_kv_row_stride("k", k_strides)) != RA_OK) return st;
-  if ((st = check_kv_row_stride("v", v_strides)) != RA_OK) return st;
+  if ((st = check_tile_row_stride("k", k_strides)) != RA_OK) return st;
+  if ((st = check_tile_row_stride("v", v_strides)) != RA_OK) return st;
 
   FoldParams p = {};
   p.q = q;
@@ -664,6 +667,8 @@ RA_API ra_status_t ra_ring_backward(const void* q, const int64_t q_strides[3], c
   if (!valid_layout((int)layout)) return fail(RA_E_INVALID_ARG, "unknown causal layout %d", (int)layout);
   if ((st = check_causal((int)layout, P, N)) != RA_OK) return st;
   if ((st = check_tensor("dout", dout, dout_strides, dt)) != RA_OK) return st;
+  if ((st = check_tile_row_stride("q", q_strides)) != RA_OK) return st;
+  if ((st = check_tile_row_stride("dout", dout_strides)) != RA_OK) return st;
   if ((st = check_tensor("dq", dq, dq_strides, dt)) != RA_OK) return st;
   if ((st = check_tensor("dk", dk, dk_strides, dt)) != RA_OK) return st;
   if ((st = check_tensor("dv", dv, dv_strides, dt)) != RA_OK) return st;

@@ -19,8 +19,10 @@
  *   * Tensors q, k, v, out have logical shape [B, H, rows, d] with the d axis
  *     contiguous; their strides are given in ELEMENTS as {batch, head, row}.
  *     Every such pointer must be 16-byte aligned and every stride a multiple of
- *     8 elements (bf16) or 4 elements (fp32); the row strides of k and v must be
- *     below 2^24 elements (RA_E_UNSUPPORTED otherwise).
+ *     8 elements (bf16) or 4 elements (fp32); the row strides of k and v (and,
+ *     for ra_ring_backward, of q and dout) must be below 2^24 elements
+ *     (RA_E_UNSUPPORTED otherwise): those rows stream through LDS tiles
+ *     addressed with 32-bit offsets.
  *   * The running state is float32 and contiguous: m, l are [B, H, rows]; o is
  *     [B, H, rows, d].  m is in natural-log units of the scaled scores, exactly
  *     as the pages define it, so it can be compared with any reference.

@@ -76,6 +76,8 @@ def _fold(lib, q=A, qs=S_BF16, k=A, ks=S_BF16, v=A, vs=S_BF16, dt=BF16, B=1, H=1
     (dict(vs=(ctypes.c_int64 * 3)(16, 8, 4)), 1, "multiple of 8"),
     (dict(m=ctypes.c_void_p(None)), 1, "NULL"),
     (dict(o=ctypes.c_void_p(0x10004)), 1, "o is not 16-byte aligned"),
+    (dict(ks=(ctypes.c_int64 * 3)(1 << 35, 1 << 34, 1 << 24)), 2, "k row stride"),
+    (dict(vs=(ctypes.c_int64 * 3)(1 << 35, 1 << 34, 1 << 24)), 2, "v row stride"),
 ])
 def test_fold_block_rejects(lib, kwargs, status, needle):
     assert _fold(lib, **kwargs) == status
@@ -197,9 +199,9 @@ def test_ring_forward_causal_rejects(lib, kwargs, status, needle):
     assert needle in lib.ra_last_error().decode()
 
 
-def _bwd(lib, lse=A, dout=A, layout=0, N=4096, P=4, ws=None, ws_bytes=0, d=128):
+def _bwd(lib, lse=A, dout=A, layout=0, N=4096, P=4, ws=None, ws_bytes=0, d=128, qs=S_BF16, ds=S_BF16):
     S = S_BF16
-    return lib.ra_ring_backward(A, S, A, S, A, S, A, S, dout, S, lse, A, S, A, S, A, S, BF16, 1, 16, N, d, P, None,
+    return lib.ra_ring_backward(A, qs, A, S, A, S, A, S, dout, ds, lse, A, S, A, S, A, S, BF16, 1, 16, N, d, P, None,
                                 P, ctypes.c_float(0.0), layout, ws if ws is not None else ctypes.c_void_p(None),
                                 ws_bytes, None)
 
@@ -212,6 +214,9 @@ def _bwd(lib, lse=A, dout=A, layout=0, N=4096, P=4, ws=None, ws_bytes=0, d=128):
     (dict(layout=3, N=4100), 1, "multiple of 2P"),
     (dict(d=96), 2, "head dim"),
     (dict(ws=ctypes.c_void_p(0x10000), ws_bytes=4096), 1, "smaller than"),
+    # Q and dO rows are streamed through LDS tiles in the dK/dV kernel
+    (dict(qs=(ctypes.c_int64 * 3)(1 << 35, 1 << 34, 1 << 24)), 2, "q row stride"),
+    (dict(ds=(ctypes.c_int64 * 3)(1 << 35, 1 << 34, 1 << 24)), 2, "dout row stride"),
 ])
 def test_ring_backward_rejects(lib, kwargs, status, needle):
     assert _bwd(lib, **kwargs) == status

@@ -142,3 +142,18 @@ def test_ring_backward_caller_workspace_and_determinism(ra):
         assert torch.equal(x, y)
     with pytest.raises(ra.RaError):
         ra.ra_ring_backward(q, k, v, out, do, lse, P, workspace=ws[:-256])
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_ring_backward_strided_layout(ra, d):
+    """Q, K, V, dO stored [B, N, H, d] and viewed as [B, H, N, d] (row stride
+    H d), so every streamed LDS tile -- K and V in the dQ kernel, Q, dO and
+    the V rows in the dK/dV kernel -- is gathered with a non-trivial row
+    stride; gradients written into contiguous tensors."""
+    B, H, N, P = 1, 8, 700, 3
+    _say(f"ring backward strided [B,N,H,d] views d={d}")
+    gen = torch.Generator(device="cuda").manual_seed(101 + d)
+    base = [torch.randn((B, N, H, d), generator=gen, device="cuda").to(torch.bfloat16) for _ in range(4)]
+    q, k, v, do = (t.permute(0, 2, 1, 3) for t in base)
+    assert q.stride(2) == H * d
+    _check_backward(ra, q, k, v, do, P, None, "bf16", f"strided d={d}")
