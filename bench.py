@@ -7,7 +7,7 @@ query block, including the final normalisation.  Inputs are resident in HBM
 before timing starts.  Prints ONE JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
-                    [--causal contiguous|striped|zigzag] [--backward]
+                    [--causal contiguous|striped|zigzag] [--backward] [--graph]
                     [--no-cpu-baseline] [--cpu-seconds S]
 
 The default workload is the 128K-token ring (B1 H32 d128 N131072 P16, all 16
@@ -16,7 +16,11 @@ as dealt to the devices in that token layout and the causal ring runs; its
 TFLOP/s count only the visible (query, key) pairs, 4 d FLOP each.  With
 --backward one step is one ra_ring_backward (dQ, dK, dV on the same ring; the
 forward that gives O and the log-sum-exp runs once, untimed), counted as the
-five products of the backward, 10 d FLOP per (query, key) pair.
+five products of the backward, 10 d FLOP per (query, key) pair.  With --graph
+the step is captured once into a HIP graph (stream capture: fold launches,
+hand-off copies, side stream and events all become nodes) and the timed steps
+are graph replays; the fold-launch times in `roofline` then come from eager
+steps.
 """
 
 from __future__ import annotations
@@ -136,6 +140,8 @@ def main() -> int:
     ap.add_argument("--backward", action="store_true", help="time the ring backward instead of the forward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step into a HIP graph (stream capture) and time its replays")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 1 GiB device copy (a known-size reference for HBM byte counters)")
     args = ap.parse_args()
@@ -195,17 +201,38 @@ def main() -> int:
     torch.cuda.synchronize()
     print("[bench] warmup done", file=sys.stderr, flush=True)
 
-    ra.ra_profile_folds(True)
+    run_step = step
+    if args.graph:
+        # The fold launches are timed on eager steps; the step time on replays.
+        ra.ra_profile_folds(True)
+        prof_steps = max(1, min(args.steps, 3))
+        for _ in range(prof_steps):
+            step()
+        torch.cuda.synchronize()
+        launches, fold_ms_total, fold_ms_max = ra.ra_profile_read()
+        ra.ra_profile_folds(False)
+        launches = launches * args.steps / prof_steps
+        fold_ms_total = fold_ms_total * args.steps / prof_steps
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+        run_step = graph.replay
+        print("[bench] step captured into a HIP graph", file=sys.stderr, flush=True)
+    else:
+        ra.ra_profile_folds(True)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for _ in range(args.steps):
-        step()
+        run_step()
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
-    launches, fold_ms_total, fold_ms_max = ra.ra_profile_read()
-    ra.ra_profile_folds(False)
+    if not args.graph:
+        launches, fold_ms_total, fold_ms_max = ra.ra_profile_read()
+        ra.ra_profile_folds(False)
     print(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
 
     pairs = (w.flops() / (4.0 * w.d)) if not args.causal else _visible_pairs(w, args.causal)
@@ -245,7 +272,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "P": w.P, "b": w.b,
                    "resident_query_blocks": w.n_q, "seed": w.seed, "causal": args.causal or False,
-                   "pass": "backward" if args.backward else "forward"},
+                   "pass": "backward" if args.backward else "forward",
+                   "launch": "hip-graph" if args.graph else "eager"},
         "pct_mfma_peak": round(100.0 * tflops / peak, 2),
         "exps_per_s": pairs * (2.0 if args.backward else 1.0) / (ms * 1e-3),
         "roofline": roofline,
