@@ -20,7 +20,9 @@ five products of the backward, 10 d FLOP per (query, key) pair.  With --graph
 the step is captured once into a HIP graph (stream capture: fold launches,
 hand-off copies, side stream and events all become nodes) and the timed steps
 are graph replays; the fold-launch times in `roofline` then come from eager
-steps.
+steps.  `clock` is the shader clock the driver reported while the timed steps
+ran (sampled from pp_dpm_sclk by a host thread) and the step throughput as a
+share of the peak scaled to that clock (null where the file is not readable).
 """
 
 from __future__ import annotations
@@ -129,6 +131,60 @@ def cpu_baseline(w, q, k, v, seconds: float) -> dict:
     }
 
 
+class ClockSampler:
+    """Samples the shader clock the driver reports (the starred level of
+    pp_dpm_sclk, in MHz) from a host thread while the timed steps run; reads
+    a sysfs file only, never the GPU."""
+
+    def __init__(self, period_s: float = 0.02):
+        import glob
+        import threading
+
+        paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.path = paths[0] if paths else None
+        self.period = period_s
+        self.samples: list[float] = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        try:
+            with open(self.path) as f:
+                for line in f:
+                    if line.rstrip().endswith("*"):
+                        return float(line.split(":")[1].strip().split("M")[0])
+        except (OSError, ValueError, IndexError):
+            return None
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            mhz = self._read()
+            if mhz is not None:
+                self.samples.append(mhz)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self.path is not None:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread.is_alive():
+            self._thread.join()
+
+    def summary(self, value: float, peak: float) -> dict | None:
+        if not self.samples:
+            return None
+        med = float(sorted(self.samples)[len(self.samples) // 2])
+        # the published peak holds at the 2.4 GHz maximum shader clock
+        at_clock = peak * med / 2400.0
+        return {"source": "pp_dpm_sclk", "median_mhz": med, "min_mhz": min(self.samples),
+                "max_mhz": max(self.samples), "samples": len(self.samples),
+                "peak_at_clock": round(at_clock, 1), "pct_peak_at_clock": round(100.0 * value / at_clock, 2)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -224,11 +280,12 @@ def main() -> int:
         ra.ra_profile_folds(True)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    start.record()
-    for _ in range(args.steps):
-        run_step()
-    end.record()
-    torch.cuda.synchronize()
+    with ClockSampler() as clock:
+        start.record()
+        for _ in range(args.steps):
+            run_step()
+        end.record()
+        torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
     if not args.graph:
         launches, fold_ms_total, fold_ms_max = ra.ra_profile_read()
@@ -277,6 +334,7 @@ def main() -> int:
         "pct_mfma_peak": round(100.0 * tflops / peak, 2),
         "exps_per_s": pairs * (2.0 if args.backward else 1.0) / (ms * 1e-3),
         "roofline": roofline,
+        "clock": clock.summary(tflops, peak),
     }
     if not args.no_cpu_baseline:
         print(f"[bench] timing the CPU oracle for ~{args.cpu_seconds:.0f} s", file=sys.stderr, flush=True)
