@@ -7,11 +7,14 @@
 // l' = alpha l + sum exp(s - m'), o' = alpha o + sum exp(s - m') v.
 //
 // Mapping onto CDNA4:
-//  * A workgroup is 4 waves; each wave owns 32 query rows, so a workgroup owns
-//    a 128-row query tile.  Q stays in registers as MFMA operands for the whole
-//    launch; the state (m, l, o) is loaded once, kept in registers while the
-//    visiting block streams past, and stored once (or normalised and written as
-//    the output on the last ring step).
+//  * A workgroup is NW waves (8 for d = 128, 4 for d = 64 and 256); each wave
+//    owns 32 query rows, so a workgroup owns a 32 NW-row query tile, and every
+//    K/V tile brought into LDS (and through L2) serves all of them.  With 8
+//    waves one workgroup fills a CU at two waves per SIMD.  Q stays in
+//    registers as MFMA operands for the whole launch; the state (m, l, o) is
+//    loaded once, kept in registers while the visiting block streams past, and
+//    stored once (or normalised and written as the output on the last ring
+//    step).
 //  * The visiting block streams through two LDS buffers in 64-key tiles (32 for
 //    d = 256): K and V row-major, the 16-byte units of each row XOR-swizzled so
 //    both read patterns below are free of bank conflicts, filled straight from
@@ -68,8 +71,8 @@ struct TileCfg {
 // in a loop unrolled by two, so both LDS buffers have compile-time offsets; a
 // ragged last tile runs once after it, with key masking.  The per-wave state
 // is written for G groups of 32 query rows; one group per wave is used.
-template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1 : 2)))
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1 : 2)))
 void fold_bf16_kernel(const FoldParams p) {
   constexpr int G = 1;  // query groups of 32 rows per wave
   constexpr int TK = TileCfg<D>::TK;
@@ -78,9 +81,9 @@ void fold_bf16_kernel(const FoldParams p) {
   constexpr int NDB = D / 32;
   constexpr int UPR = D / 8;
   constexpr int TE = TK * D;
-  constexpr int CPW = TE / 512 / 4;
-  constexpr int QT = 4 * 32 * G;  // query rows per workgroup
-  static_assert(CPW >= 1 && TE % 2048 == 0, "tile must split into whole 1 KB chunks per wave");
+  constexpr int CPW = TE / 512 / NW;
+  constexpr int QT = NW * 32 * G;  // query rows per workgroup
+  static_assert(CPW >= 1 && TE % (512 * NW) == 0, "tile must split into whole 1 KB chunks per wave");
   __shared__ __attribute__((aligned(1024))) __bf16 lds[2 * 2 * TE];
 
   const int tiles_q = (p.q_rows + QT - 1) / QT;
@@ -390,22 +393,25 @@ void fold_bf16_kernel(const FoldParams p) {
 
 }  // namespace
 
+// Waves per workgroup of the d-specialised kernel.
+constexpr int waves_for(int d) { return d == 128 ? 8 : 4; }
+
 hipError_t launch_fold_bf16(const FoldParams& p, int d, hipStream_t s) {
-  constexpr int rows_per_wg = 4 * 32;
+  const int rows_per_wg = waves_for(d) * 32;
   const int64_t tiles_q = (p.q_rows + rows_per_wg - 1) / rows_per_wg;
   const int64_t grid = tiles_q * p.n_res * p.H * p.B;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  const dim3 gd((unsigned)grid), bd(256);
+  const dim3 gd((unsigned)grid), bd(waves_for(d) * 64);
   switch (d) {
     case 64:
-      fold_bf16_kernel<64><<<gd, bd, 0, s>>>(p);
+      fold_bf16_kernel<64, waves_for(64)><<<gd, bd, 0, s>>>(p);
       break;
     case 128:
-      fold_bf16_kernel<128><<<gd, bd, 0, s>>>(p);
+      fold_bf16_kernel<128, waves_for(128)><<<gd, bd, 0, s>>>(p);
       break;
     case 256:
-      fold_bf16_kernel<256><<<gd, bd, 0, s>>>(p);
+      fold_bf16_kernel<256, waves_for(256)><<<gd, bd, 0, s>>>(p);
       break;
     default:
       return hipErrorInvalidValue;
