@@ -8,7 +8,9 @@
 // to the visiting block's dK_j, dV_j, which travel with the block.
 //
 // Two kernels per step, no atomics:
-//  * bwd_dq_kernel: like the forward fold -- 4 waves x 32 query rows, Q and dO
+// Both run NW waves per workgroup (8 for d = 128, 4 for d = 64 and 256), so a
+// tile streamed through L2 into LDS serves 32 NW rows (keys).
+//  * bwd_dq_kernel: like the forward fold -- NW waves x 32 query rows, Q and dO
 //    in registers as MFMA B operands, the visiting K and V streamed through
 //    double-buffered swizzled LDS in 32-key tiles.  S^T = K Q^T and
 //    dP^T = V dO^T put one query row in each lane (lane ^ 32 holds the other
@@ -18,11 +20,11 @@
 //  * bwd_dkdv_kernel: the transpose of the same pattern -- each wave owns 32
 //    keys (K in registers, the workgroup's V rows in LDS, both as B operands)
 //    and streams the resident block's Q and dO rows (plus their L and D)
-//    through LDS in 32-row tiles;
-//    S = Q K^T and dP = dO V^T put one key in each lane, and
+//    through LDS in 32-row tiles; S = Q K^T and dP = dO V^T put one key in
+//    each lane, and
 //    dV^T += dO^T P, dK^T += Q^T dS read dO^T and Q^T by transposed LDS
 //    reads.  The dK, dV accumulators (fp32, unscaled by s) are loaded and
-//    stored once per launch; one workgroup owns each 128-key tile, so no two
+//    stored once per launch; one workgroup owns each 32 NW-key tile, so no two
 //    workgroups touch the same rows.  Keeping V in LDS rather than registers
 //    leaves the d <= 128 kernel within 256 VGPRs: two waves per SIMD, and the
 //    MFMA accumulators stay in VGPRs where the VALU reads them directly.
@@ -111,17 +113,17 @@ __device__ __forceinline__ bf16x8 tr_operand(const __bf16* rows16, int off0, int
 }
 
 // ---------------------------------------------------------------------------
-// dQ: one workgroup per 128 query rows of one resident block.
-template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1 : 2)))
+// dQ: one workgroup per 32 NW query rows of one resident block.
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1 : 2)))
 void bwd_dq_kernel(const BwdParams p) {
   constexpr int TK = 32;
   constexpr int NC = D / 16;
   constexpr int NDB = D / 32;
   constexpr int TE = TK * D;
-  constexpr int CPW = TE / 512 / 4;
-  constexpr int QT = 128;
-  static_assert(CPW >= 1 && TE % 2048 == 0, "tile must split into whole 1 KB chunks per wave");
+  constexpr int CPW = TE / 512 / NW;
+  constexpr int QT = NW * 32;
+  static_assert(CPW >= 1 && TE % (512 * NW) == 0, "tile must split into whole 1 KB chunks per wave");
   __shared__ __attribute__((aligned(1024))) __bf16 lds[2 * 2 * TE];  // [buffer][K | V][TK][D]
 
   const int tiles_q = (p.q_rows + QT - 1) / QT;
@@ -295,17 +297,17 @@ void bwd_dq_kernel(const BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: one workgroup per 128 keys of one visiting block.
-template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1 : 2)))
+// dK, dV: one workgroup per 32 NW keys of one visiting block.
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1 : 2)))
 void bwd_dkdv_kernel(const BwdParams p) {
   constexpr int TQ = 32;
   constexpr int NC = D / 16;
   constexpr int NDB = D / 32;
   constexpr int TE = TQ * D;
-  constexpr int CPW = TE / 512 / 4;
-  constexpr int KT = 128;
-  static_assert(CPW >= 1 && TE % 2048 == 0, "tile must split into whole 1 KB chunks per wave");
+  constexpr int CPW = TE / 512 / NW;
+  constexpr int KT = NW * 32;
+  static_assert(CPW >= 1 && TE % (512 * NW) == 0, "tile must split into whole 1 KB chunks per wave");
   __shared__ __attribute__((aligned(1024))) __bf16 lds[2 * 2 * TE];  // [buffer][Q | dO][TQ][D]
   __shared__ __attribute__((aligned(16))) float lrow[2][2 * TQ];     // [buffer][nl2 of TQ rows | dd of TQ rows]
   __shared__ __attribute__((aligned(1024))) __bf16 vlds[KT * D];     // V rows of the workgroup's keys
@@ -494,19 +496,23 @@ void bwd_dkdv_kernel(const BwdParams p) {
 
 }  // namespace
 
+// Waves per workgroup of the d-specialised backward kernels.
+constexpr int bwd_waves(int d) { return d == 128 ? 8 : 4; }
+
 hipError_t launch_bwd_dq_bf16(const BwdParams& p, int d, hipStream_t s) {
-  const int64_t grid = (int64_t)((p.q_rows + 127) / 128) * p.n_res * p.H * p.B;
+  const int64_t grid = (int64_t)((p.q_rows + bwd_waves(d) * 32 - 1) / (bwd_waves(d) * 32)) * p.n_res * p.H * p.B;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  const dim3 gd((unsigned)grid), bd(bwd_waves(d) * 64);
   switch (d) {
     case 64:
-      bwd_dq_kernel<64><<<dim3((unsigned)grid), dim3(256), 0, s>>>(p);
+      bwd_dq_kernel<64, bwd_waves(64)><<<gd, bd, 0, s>>>(p);
       break;
     case 128:
-      bwd_dq_kernel<128><<<dim3((unsigned)grid), dim3(256), 0, s>>>(p);
+      bwd_dq_kernel<128, bwd_waves(128)><<<gd, bd, 0, s>>>(p);
       break;
     case 256:
-      bwd_dq_kernel<256><<<dim3((unsigned)grid), dim3(256), 0, s>>>(p);
+      bwd_dq_kernel<256, bwd_waves(256)><<<gd, bd, 0, s>>>(p);
       break;
     default:
       return hipErrorInvalidValue;
@@ -515,18 +521,19 @@ hipError_t launch_bwd_dq_bf16(const BwdParams& p, int d, hipStream_t s) {
 }
 
 hipError_t launch_bwd_dkdv_bf16(const BwdParams& p, int d, hipStream_t s) {
-  const int64_t grid = (int64_t)((p.kv_rows + 127) / 128) * p.n_res * p.H * p.B;
+  const int64_t grid = (int64_t)((p.kv_rows + bwd_waves(d) * 32 - 1) / (bwd_waves(d) * 32)) * p.n_res * p.H * p.B;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  const dim3 gd((unsigned)grid), bd(bwd_waves(d) * 64);
   switch (d) {
     case 64:
-      bwd_dkdv_kernel<64><<<dim3((unsigned)grid), dim3(256), 0, s>>>(p);
+      bwd_dkdv_kernel<64, bwd_waves(64)><<<gd, bd, 0, s>>>(p);
       break;
     case 128:
-      bwd_dkdv_kernel<128><<<dim3((unsigned)grid), dim3(256), 0, s>>>(p);
+      bwd_dkdv_kernel<128, bwd_waves(128)><<<gd, bd, 0, s>>>(p);
       break;
     case 256:
-      bwd_dkdv_kernel<256><<<dim3((unsigned)grid), dim3(256), 0, s>>>(p);
+      bwd_dkdv_kernel<256, bwd_waves(256)><<<gd, bd, 0, s>>>(p);
       break;
     default:
       return hipErrorInvalidValue;

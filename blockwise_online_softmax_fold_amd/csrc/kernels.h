@@ -104,8 +104,8 @@ __host__ __device__ inline int32_t last_key_at_or_before(int mode, int32_t P, in
 }
 
 // One backward launch over n_res (resident query block, visiting block) pairs
-// of one ring step.  The dQ pass (one workgroup per 128 query rows) folds the
-// visiting block into dQ; the dK/dV pass (one workgroup per 128 keys) adds the
+// of one ring step.  The dQ pass (one workgroup per tile of query rows) folds
+// the visiting block into dQ; the dK/dV pass (one workgroup per tile of keys) adds the
 // resident block's share to the visiting block's dK, dV accumulators.  Row
 // arrays (nl2, dd, dq_acc) follow the resident rows like the forward state;
 // dk_acc, dv_acc are [B, H, N, d] over the whole sequence.
