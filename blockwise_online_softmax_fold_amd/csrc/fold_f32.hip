@@ -6,9 +6,10 @@
 // the online-softmax identity (m' = max(m, max s), alpha = exp(m - m'),
 // l' = alpha l + sum exp(s - m'), o' = alpha o + sum exp(s - m') v).
 //
-// Layout: TPR = d / 64 threads share one query row, each holding 64 of its q
-// and o columns in registers; partial dot products are combined across those
-// lanes with xor shuffles.  K and V stream through LDS in 32-key tiles, which
+// Layout: TPR = d / CPL threads share one query row, each holding CPL of its
+// q and o columns in registers; partial dot products are combined across
+// those lanes with xor shuffles.  A small CPL (8 for d = 64, 16 above) keeps
+// the serial work per lane short and the workgroup count up on small rings.  K and V stream through LDS in 32-key tiles, which
 // every row of the workgroup reads as broadcasts.
 //
 // Causal masking (math page, "Causal masking, load balance, and other
@@ -28,9 +29,9 @@ constexpr int kTileK = 32;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-template <int D>
+template <int D, int CPL>
 __global__ __launch_bounds__(256) void fold_f32_kernel(const FoldParams p) {
-  constexpr int TPR = D / 64;     // threads per query row
+  constexpr int TPR = D / CPL;    // threads per query row
   constexpr int ROWS = 256 / TPR; // query rows per workgroup
   constexpr int C4 = D / 4;       // float4 chunks per K/V row
   __shared__ __attribute__((aligned(16))) float ks[kTileK * D];
@@ -68,13 +69,13 @@ __global__ __launch_bounds__(256) void fold_f32_kernel(const FoldParams p) {
     if (kv_vis == 0 && p.flags == (kLoadState | kStoreState)) return;
   }
   const int64_t srow = (int64_t)p.q_row0[r] + (row_ok ? row : q_len - 1);
-  const int col0 = 64 * sub;
+  const int col0 = CPL * sub;
 
-  float qv[64];
+  float qv[CPL];
   {
     const float* qp = (const float*)p.q + bi * p.q_sb + hi * p.q_sh + srow * p.q_sr + col0;
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
+    for (int c = 0; c < CPL / 4; ++c) {
       const f32x4 t = *(const f32x4*)(qp + 4 * c);
 #pragma unroll
       for (int e = 0; e < 4; ++e) qv[4 * c + e] = t[e];
@@ -83,14 +84,14 @@ __global__ __launch_bounds__(256) void fold_f32_kernel(const FoldParams p) {
 
   const int64_t st_row = ((int64_t)bi * p.H + hi) * p.st_bh + srow;
   float mc, l, m_in;
-  float ov[64];
+  float ov[CPL];
   if (p.flags & kLoadState) {
     m_in = p.m[st_row];
     mc = m_in * kLog2e;
     l = p.l[st_row];
     const float* op = p.o + st_row * D + col0;
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
+    for (int c = 0; c < CPL / 4; ++c) {
       const f32x4 t = *(const f32x4*)(op + 4 * c);
 #pragma unroll
       for (int e = 0; e < 4; ++e) ov[4 * c + e] = t[e];
@@ -100,7 +101,7 @@ __global__ __launch_bounds__(256) void fold_f32_kernel(const FoldParams p) {
     mc = -INFINITY;
     l = 0.0f;
 #pragma unroll
-    for (int c = 0; c < 64; ++c) ov[c] = 0.0f;
+    for (int c = 0; c < CPL; ++c) ov[c] = 0.0f;
   }
 
   const float* kbase = (const float*)p.k + bi * p.k_sb + hi * p.k_sh + p.k_off[r];
@@ -126,7 +127,7 @@ __global__ __launch_bounds__(256) void fold_f32_kernel(const FoldParams p) {
       const float* kr = ks + j * D + col0;
       float acc = 0.0f;
 #pragma unroll
-      for (int c = 0; c < 64; ++c) acc = fmaf(qv[c], kr[c], acc);
+      for (int c = 0; c < CPL; ++c) acc = fmaf(qv[c], kr[c], acc);
 #pragma unroll
       for (int x = 1; x < TPR; x <<= 1) acc += __shfl_xor(acc, x);
       s[j] = key0 + j <= lim ? acc : -INFINITY;
@@ -148,12 +149,12 @@ __global__ __launch_bounds__(256) void fold_f32_kernel(const FoldParams p) {
     }
     l = fmaf(l, alpha, lsum);
 #pragma unroll
-    for (int c = 0; c < 64; ++c) ov[c] *= alpha;
+    for (int c = 0; c < CPL; ++c) ov[c] *= alpha;
 #pragma unroll
     for (int j = 0; j < kTileK; ++j) {
       const float* vr = vs + j * D + col0;
 #pragma unroll
-      for (int c = 0; c < 64; ++c) ov[c] = fmaf(s[j], vr[c], ov[c]);
+      for (int c = 0; c < CPL; ++c) ov[c] = fmaf(s[j], vr[c], ov[c]);
     }
   }
 
@@ -163,7 +164,7 @@ __global__ __launch_bounds__(256) void fold_f32_kernel(const FoldParams p) {
     if (p.lse != nullptr && sub == 0) p.lse[st_row] = l > 0.0f ? (mc + log2f(l)) * kLn2 : -INFINITY;
     float* op = (float*)p.out + bi * p.out_sb + hi * p.out_sh + srow * p.out_sr + col0;
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
+    for (int c = 0; c < CPL / 4; ++c) {
       f32x4 t;
 #pragma unroll
       for (int e = 0; e < 4; ++e) t[e] = ov[4 * c + e] * inv;
@@ -178,7 +179,7 @@ __global__ __launch_bounds__(256) void fold_f32_kernel(const FoldParams p) {
     }
     float* op = p.o + st_row * D + col0;
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
+    for (int c = 0; c < CPL / 4; ++c) {
       f32x4 t;
 #pragma unroll
       for (int e = 0; e < 4; ++e) t[e] = ov[4 * c + e];
@@ -189,21 +190,24 @@ __global__ __launch_bounds__(256) void fold_f32_kernel(const FoldParams p) {
 
 }  // namespace
 
+// Columns of q and o per lane.
+constexpr int cols_per_lane(int d) { return d == 64 ? 8 : 16; }
+
 hipError_t launch_fold_f32(const FoldParams& p, int d, hipStream_t s) {
-  const int rows_per_wg = 256 / (d / 64);
+  const int rows_per_wg = 256 / (d / cols_per_lane(d));
   const int64_t tiles_q = (p.q_rows + rows_per_wg - 1) / rows_per_wg;
   const int64_t grid = tiles_q * p.n_res * p.H * p.B;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   switch (d) {
     case 64:
-      fold_f32_kernel<64><<<dim3((unsigned)grid), dim3(256), 0, s>>>(p);
+      fold_f32_kernel<64, cols_per_lane(64)><<<dim3((unsigned)grid), dim3(256), 0, s>>>(p);
       break;
     case 128:
-      fold_f32_kernel<128><<<dim3((unsigned)grid), dim3(256), 0, s>>>(p);
+      fold_f32_kernel<128, cols_per_lane(128)><<<dim3((unsigned)grid), dim3(256), 0, s>>>(p);
       break;
     case 256:
-      fold_f32_kernel<256><<<dim3((unsigned)grid), dim3(256), 0, s>>>(p);
+      fold_f32_kernel<256, cols_per_lane(256)><<<dim3((unsigned)grid), dim3(256), 0, s>>>(p);
       break;
     default:
       return hipErrorInvalidValue;
