@@ -157,3 +157,13 @@ def test_ring_backward_strided_layout(ra, d):
     q, k, v, do = (t.permute(0, 2, 1, 3) for t in base)
     assert q.stride(2) == H * d
     _check_backward(ra, q, k, v, do, P, None, "bf16", f"strided d={d}")
+
+
+@pytest.mark.parametrize("layout", [None, "striped"])
+def test_ring_backward_many_devices(ra, layout):
+    """P = 70 devices: more resident blocks than one backward launch takes (64),
+    so each step's dQ and dK/dV passes are split into two launches."""
+    N, P, d = 280, 70, 64
+    _say(f"ring backward P={P} N={N} layout={layout}")
+    q, k, v, do = _inputs(1, 2, N, d, "bf16", 111)
+    _check_backward(ra, q, k, v, do, P, layout, "bf16", f"P={P} {layout}")

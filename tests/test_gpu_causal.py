@@ -198,3 +198,14 @@ def test_ring_causal_16k(ra, layout):
     for hi in (0, H - 1):
         ref = oracle.dense_attention(q[0, hi, rows], k[0, hi], v[0, hi], q_pos=pos[rows], k_pos=pos)
         check_output(got[0, hi, rows], ref, "bf16", f"causal 16K head {hi}")
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_ring_causal_many_devices(ra, layout):
+    """P = 70 devices of 4 rows: more resident blocks than one fold launch takes
+    (64), so every ring step is split into two launches."""
+    P, b, d = 70, 4, 64
+    _say(f"ring causal P={P} b={b} layout={layout}")
+    got, q, k, v, pos, qb = _causal_ring_case(ra, layout, "bf16", 1, 2, P, b, d, None, 303)
+    ref = oracle.dense_attention(q, k, v, q_pos=pos, k_pos=pos)
+    check_output(got, ref, "bf16", f"causal ring P={P} {layout}")
