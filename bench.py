@@ -119,6 +119,23 @@ def cpu_baseline(w, q, k, v, seconds: float) -> dict:
         rows_done += qs.shape[0]
         r0 = (r0 + chunk) % q64.shape[0]
     flops = 4.0 * rows_done * w.N * w.d
+    # the naive ring loop (init, P folds in ring order, finalize) on rows of
+    # query block 0, for about a third of the time
+    from oracle import ring as oring
+
+    bounds = oring.block_bounds(w.N, w.P)
+    q0 = q64[bounds[0][0]:bounds[0][1]]
+    ring_rows, ring_elapsed, r0 = 0, 0.0, 0
+    while ring_elapsed < seconds / 3 and ring_rows < q0.shape[0]:
+        qs = q0[r0:r0 + chunk]
+        t0 = time.perf_counter()
+        st = oring.init_state((), qs.shape[0], w.d)
+        for j in oring.ring_schedule(w.P, 0):
+            st = oring.fold(st, qs, k64[bounds[j][0]:bounds[j][1]], v64[bounds[j][0]:bounds[j][1]])
+        oring.finalize(st)
+        ring_elapsed += time.perf_counter() - t0
+        ring_rows += qs.shape[0]
+        r0 = (r0 + chunk) % q0.shape[0]
     del np
     return {
         "value": flops / elapsed / 1e12,
@@ -127,6 +144,9 @@ def cpu_baseline(w, q, k, v, seconds: float) -> dict:
         "kind": "oracle",
         "sample": f"fp64 dense oracle, {rows_done} query rows x {w.N} keys x d={w.d} of head 0 "
                   f"({elapsed:.1f} s; full workload is {w.B * w.H * w.n_q * w.b} rows)",
+        "ring_loop": {"value": 4.0 * ring_rows * w.N * w.d / ring_elapsed / 1e12, "unit": "TFLOP/s",
+                      "sample": f"fp64 naive ring loop, {ring_rows} rows of query block 0 folding all "
+                                f"{w.P} blocks ({ring_elapsed:.1f} s)"},
         "host_cpus": len(os.sched_getaffinity(0)),
     }
 
