@@ -144,6 +144,7 @@ def cpu_baseline(w, q, k, v, seconds: float) -> dict:
         "kind": "oracle",
         "sample": f"fp64 dense oracle, {rows_done} query rows x {w.N} keys x d={w.d} of head 0 "
                   f"({elapsed:.1f} s; full workload is {w.B * w.H * w.n_q * w.b} rows)",
+        "full_workload_s_extrapolated": round(w.flops() / (flops / elapsed), 1),
         "ring_loop": {"value": 4.0 * ring_rows * w.N * w.d / ring_elapsed / 1e12, "unit": "TFLOP/s",
                       "sample": f"fp64 naive ring loop, {ring_rows} rows of query block 0 folding all "
                                 f"{w.P} blocks ({ring_elapsed:.1f} s)"},
