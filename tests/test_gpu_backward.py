@@ -167,3 +167,17 @@ def test_ring_backward_many_devices(ra, layout):
     _say(f"ring backward P={P} N={N} layout={layout}")
     q, k, v, do = _inputs(1, 2, N, d, "bf16", 111)
     _check_backward(ra, q, k, v, do, P, layout, "bf16", f"P={P} {layout}")
+
+
+@pytest.mark.parametrize("layout", [None, "zigzag"])
+def test_ring_backward_explicit_scale(ra, layout):
+    """A caller-given scale through ra_ring_forward_ex and ra_ring_backward, B = 2."""
+    N, P, d, sc = 512, 4, 128, 0.25
+    _say(f"ring backward explicit scale={sc} layout={layout}")
+    q, k, v, do = _inputs(2, 2, N, d, "bf16", 121)
+    out, lse = ra.ra_ring_forward_ex(q, k, v, P, layout, scale=sc)
+    dq, dk, dv = ra.ra_ring_backward(q, k, v, out, do, lse, P, layout, scale=sc)
+    torch.cuda.synchronize()
+    want = ob.ring_attention_backward(to64(q), to64(k), to64(v), to64(do), P, scale=sc, causal_layout=layout)
+    for name, g, w in zip(("dQ", "dK", "dV"), (dq, dk, dv), want):
+        check_grad(g, w, "bf16", f"scale={sc} {layout} {name}")

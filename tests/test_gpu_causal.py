@@ -209,3 +209,18 @@ def test_ring_causal_many_devices(ra, layout):
     got, q, k, v, pos, qb = _causal_ring_case(ra, layout, "bf16", 1, 2, P, b, d, None, 303)
     ref = oracle.dense_attention(q, k, v, q_pos=pos, k_pos=pos)
     check_output(got, ref, "bf16", f"causal ring P={P} {layout}")
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_ring_causal_batch_and_scale(ra, layout):
+    """B = 2 batches and a caller-given scale under each causal layout."""
+    B, H, P, b, d, sc = 2, 2, 4, 96, 128, 0.2
+    _say(f"ring causal B={B} scale={sc} layout={layout}")
+    N = P * b
+    gen = torch.Generator(device="cuda").manual_seed(505)
+    q, k, v = (_rand((B, H, N, d), gen, "bf16") for _ in range(3))
+    out = ra.ra_ring_forward_causal(q, k, v, P, layout, scale=sc)
+    torch.cuda.synchronize()
+    pos = layouts.positions(layout, P, b).reshape(-1)
+    ref = oracle.dense_attention(to64(q), to64(k), to64(v), scale=sc, q_pos=pos, k_pos=pos)
+    check_output(out, ref, "bf16", f"causal {layout} B={B} scale={sc}")

@@ -325,3 +325,16 @@ def test_workload_sampled(ra, wid, per_block, heads):
     assert torch.isfinite(out).all()
     vmax = v.abs().amax().float()
     assert out.float().abs().amax() <= vmax * 1.01
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64), ("bf16", 256)])
+def test_ring_forward_explicit_scale(ra, dtype, d):
+    """A caller-given softmax scale (0.3, not 1/sqrt(d)) through the ABI, B = 2,
+    against the dense oracle with the same scale."""
+    B, H, N, P, sc = 2, 2, 600, 3, 0.3
+    _say(f"ring_forward explicit scale={sc} dtype={dtype} B={B} H={H} N={N} d={d} P={P}")
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q, k, v = workloads.make_small(B, H, N, d, tdt, seed=44 + d)
+    out = ra.ra_ring_forward(q, k, v, P, scale=sc)
+    torch.cuda.synchronize()
+    check_output(out, oracle.dense_attention(to64(q), to64(k), to64(v), scale=sc), dtype, "explicit scale")
