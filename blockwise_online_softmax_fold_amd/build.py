@@ -16,6 +16,10 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libra.so")
+# the plain-C example client of the ABI (tests/c/ring_forward_c.c), built beside libra.so
+C_CLIENT_SRC = os.path.join(ROOT, "tests", "c", "ring_forward_c.c")
+C_CLIENT_PATH = os.path.join(PKG_DIR, "ring_forward_c")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 SOURCES = ["ra_api.hip", "fold_bf16.hip", "fold_f32.hip", "fold_bwd_bf16.hip", "fold_bwd_f32.hip", "state.hip"]
 ARCH = "gfx950"
 
@@ -47,8 +51,31 @@ def build_command(out_path: str, extra: list[str] | None = None) -> list[str]:
     ]
 
 
+def c_client_command(out_path: str, lib_dir: str = PKG_DIR) -> list[str]:
+    """gcc command for the plain-C client, linked against libra.so in lib_dir."""
+    cc = os.environ.get("CC") or shutil.which("gcc") or "cc"
+    return [
+        cc, "-std=c11", "-O2", "-Wall", "-D__HIP_PLATFORM_AMD__",
+        "-I", INCLUDE, "-I", os.path.join(ROCM, "include"),
+        C_CLIENT_SRC, "-o", out_path,
+        "-L", lib_dir, "-l:libra.so", "-L", os.path.join(ROCM, "lib"), "-lamdhip64",
+        f"-Wl,-rpath,{lib_dir}", "-Wl,-rpath,$ORIGIN", f"-Wl,-rpath,{os.path.join(ROCM, 'lib')}",
+    ]
+
+
+def build_c_client(verbose: bool = False) -> str:
+    """Compile the plain-C client against the in-tree libra.so."""
+    cmd = c_client_command(C_CLIENT_PATH)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"C client build failed ({res.returncode}):\n{res.stdout}\n{res.stderr}")
+    return C_CLIENT_PATH
+
+
 def build(verbose: bool = False) -> str:
-    """Compile libra.so; always recompiles.  Returns the library path."""
+    """Compile libra.so (always recompiles) and the C client.  Returns the library path."""
     tmp = LIB_PATH + f".tmp{os.getpid()}"
     cmd = build_command(tmp)
     if verbose:
@@ -59,6 +86,7 @@ def build(verbose: bool = False) -> str:
             os.remove(tmp)
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stdout}\n{res.stderr}")
     os.replace(tmp, LIB_PATH)
+    build_c_client(verbose)
     return LIB_PATH
 
 
