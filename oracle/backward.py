@@ -146,3 +146,56 @@ def _forward_block(q_i, k, v, i, blocks, scale, pos, bounds):
         qp, kp = (None, None) if pos is None else (pos[i], pos[j])
         state = fold(state, q_i, k[..., c0:c1, :], v[..., c0:c1, :], scale, qp, kp)
     return finalize(state), state
+
+
+def backward_rows(q, k, v, do, q_rows, k_rows, scale: float | None = None, row_chunk: int = 1024):
+    """Selected rows of (dQ, dK, dV) for one (batch, head) -- [N, d] inputs --
+    for checking full-size runs the dense backward cannot hold in memory.
+
+    dQ_i needs only row i: its softmax weights P_i, dP_i = dO_i V^T and
+    D_i = dO_i . O_i.  dK_j and dV_j need column j of P and dS over every
+    query row, so every row's log-sum-exp L_i and D_i are computed first in a
+    streaming pass over ``row_chunk`` query rows at a time (same formulas as
+    ``dense_attention_backward``: dV = P^T dO, dS = P * (dP - D),
+    dQ = s dS K, dK = s dS^T Q).
+    Returns (dq[len(q_rows), d], dk[len(k_rows), d], dv[len(k_rows), dv])."""
+    q, k, v, do = (_as_f64(x) for x in (q, k, v, do))
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    q_rows = np.asarray(q_rows, dtype=np.int64)
+    k_rows = np.asarray(k_rows, dtype=np.int64)
+    n = q.shape[0]
+    lse, dd = _lse_and_dd(q, k, v, do, scale, row_chunk)
+    kj = k[k_rows]
+    dk = np.zeros((len(k_rows), q.shape[1]))
+    dv = np.zeros((len(k_rows), v.shape[1]))
+    # pass 2: the chosen key rows' dK, dV over every query row
+    for a in range(0, n, row_chunk):
+        p = np.exp((q[a:a + row_chunk] @ kj.T) * scale - lse[a:a + row_chunk, None])
+        dpj = do[a:a + row_chunk] @ v[k_rows].T
+        dsj = p * (dpj - dd[a:a + row_chunk, None])
+        dv += p.T @ do[a:a + row_chunk]
+        dk += scale * dsj.T @ q[a:a + row_chunk]
+    # the chosen query rows' dQ
+    s = (q[q_rows] @ k.T) * scale
+    p = np.exp(s - lse[q_rows, None])
+    dp = do[q_rows] @ v.T
+    dq = scale * (p * (dp - dd[q_rows, None])) @ k
+    return dq, dk, dv
+
+
+def _lse_and_dd(q, k, v, do, scale, row_chunk):
+    """Pass 1 of ``backward_rows``: every query row's L_i = m_i + log l_i and
+    D_i = dO_i . O_i, ``row_chunk`` rows at a time."""
+    n = q.shape[0]
+    lse = np.empty(n)
+    dd = np.empty(n)
+    for a in range(0, n, row_chunk):
+        s = (q[a:a + row_chunk] @ k.T) * scale
+        m = s.max(axis=1, keepdims=True)
+        e = np.exp(s - m)
+        z = e.sum(axis=1, keepdims=True)
+        lse[a:a + row_chunk] = (m + np.log(z))[:, 0]
+        o = (e / z) @ v
+        dd[a:a + row_chunk] = (do[a:a + row_chunk] * o).sum(axis=1)
+    return lse, dd

@@ -181,3 +181,31 @@ def test_ring_backward_explicit_scale(ra, layout):
     want = ob.ring_attention_backward(to64(q), to64(k), to64(v), to64(do), P, scale=sc, causal_layout=layout)
     for name, g, w in zip(("dQ", "dK", "dV"), (dq, dk, dv), want):
         check_grad(g, w, "bf16", f"scale={sc} {layout} {name}")
+
+
+def test_ring_backward_128k_sampled(ra):
+    """The headline shape (B1 H32 d128 N131072 P16, all blocks resident), as
+    bench.py --backward launches it: head 0's dQ on 64 sampled query rows and
+    dK, dV on 64 sampled key rows against the oracle's streaming row sampler
+    (one full fp64 pass over head 0, about a minute of CPU time); every
+    gradient finite."""
+    import workloads
+    from tests.helpers import sample_rows
+
+    w = workloads.WORKLOADS[3]
+    _say(f"ring backward full size {w.describe()}")
+    q, k, v = workloads.make_inputs(w, device="cuda")
+    do = torch.randn(q.shape, generator=torch.Generator(device="cuda").manual_seed(w.seed + 7),
+                     device="cuda").to(q.dtype)
+    out, lse = ra.ra_ring_forward_ex(q, k, v, w.P)
+    dq, dk, dv = ra.ra_ring_backward(q, k, v, out, do, lse, w.P)
+    torch.cuda.synchronize()
+    for g in (dq, dk, dv):
+        assert torch.isfinite(g).all()
+    rows = sample_rows(w.P, w.b, 4, seed=w.seed)
+    print(f"[case] oracle pass over head 0 ({len(rows)} query and key rows)", flush=True)
+    want = ob.backward_rows(to64(q[0, 0]), to64(k[0, 0]), to64(v[0, 0]), to64(do[0, 0]), rows, rows, row_chunk=2048)
+    print("[case] oracle done", flush=True)
+    idx = torch.from_numpy(rows).cuda()
+    for name, g, ww in zip(("dQ", "dK", "dV"), (dq, dk, dv), want):
+        check_grad(g[0, 0, idx], ww, "bf16", f"128K {name}")

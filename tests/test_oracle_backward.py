@@ -143,3 +143,43 @@ def test_planted_backward_mistakes_are_caught(monkeypatch, mistake):
     monkeypatch.setattr(ob, "fold_backward", bad)
     got = ob.ring_attention_backward(q, k, v, do, 3)
     assert any(not np.allclose(g, w, atol=1e-6) for g, w in zip(got, want))
+
+
+def test_backward_rows_matches_autograd():
+    """The streaming row sampler against torch fp64 autograd on a sequence
+    long enough to need several row chunks."""
+    n, d = 300, 16
+    q, k, v, do = (_rand((n, d), s, 1.2) for s in (31, 32, 33, 34))
+    rows_q = np.array([0, 7, 150, 299])
+    rows_k = np.array([1, 64, 200, 299])
+    want = _autograd(q, k, v, do)
+    for chunk in (1024, 64, 7):
+        dq, dk, dv = ob.backward_rows(q, k, v, do, rows_q, rows_k, row_chunk=chunk)
+        np.testing.assert_allclose(dq, want[0][rows_q], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(dk, want[1][rows_k], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(dv, want[2][rows_k], rtol=0, atol=1e-12)
+    dq, dk, dv = ob.backward_rows(q, k, v, do, rows_q, rows_k, scale=0.4, row_chunk=50)
+    want = _autograd(q, k, v, do, scale=0.4)
+    np.testing.assert_allclose(dk, want[1][rows_k], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("mistake", ["no_D", "lse_without_log"])
+def test_backward_rows_planted_mistakes_are_caught(monkeypatch, mistake):
+    """Mistakes planted in the sampler's first pass fail the autograd comparison."""
+    n, d = 120, 8
+    q, k, v, do = (_rand((n, d), s) for s in (35, 36, 37, 38))
+    rows = np.array([3, 90])
+    want = _autograd(q, k, v, do)
+    real = ob._lse_and_dd
+
+    def bad(q_, k_, v_, do_, scale, chunk):
+        lse, dd = real(q_, k_, v_, do_, scale, chunk)
+        if mistake == "no_D":
+            return lse, np.zeros_like(dd)
+        s = q_ @ k_.T * scale
+        return s.max(axis=1) + (np.exp(s - s.max(axis=1, keepdims=True))).sum(axis=1), dd
+
+    monkeypatch.setattr(ob, "_lse_and_dd", bad)
+    dq, dk, dv = ob.backward_rows(q, k, v, do, rows, rows, row_chunk=32)
+    assert not (np.allclose(dq, want[0][rows], atol=1e-6) and np.allclose(dk, want[1][rows], atol=1e-6)
+                and np.allclose(dv, want[2][rows], atol=1e-6))
