@@ -224,3 +224,25 @@ def test_ring_causal_batch_and_scale(ra, layout):
     pos = layouts.positions(layout, P, b).reshape(-1)
     ref = oracle.dense_attention(to64(q), to64(k), to64(v), scale=sc, q_pos=pos, k_pos=pos)
     check_output(out, ref, "bf16", f"causal {layout} B={B} scale={sc}")
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "zigzag"])
+def test_ring_causal_128k_sampled(ra, layout):
+    """The headline shape (B1 H32 d128 N131072 P16) as bench.py --causal runs
+    it: random inputs taken as already dealt in ``layout``'s device order;
+    48 sampled rows per block of heads 0 and 31 against the dense causal
+    oracle at those rows' positions."""
+    import workloads
+
+    w = workloads.WORKLOADS[3]
+    _say(f"ring causal full size {layout} {w.describe()}")
+    q, k, v = workloads.make_inputs(w, device="cuda")
+    out = ra.ra_ring_forward_causal(q, k, v, w.P, layout)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    pos = layouts.positions(layout, w.P, w.b).reshape(-1)
+    rows = sample_rows(w.P, w.b, 48, 3003)
+    idx = torch.from_numpy(rows).cuda()
+    for hi in (0, w.H - 1):
+        ref = oracle.dense_attention(to64(q[0, hi, idx]), to64(k[0, hi]), to64(v[0, hi]), q_pos=pos[rows], k_pos=pos)
+        check_output(to64(out[0, hi, idx]), ref, "bf16", f"causal 128K {layout} head {hi}")
