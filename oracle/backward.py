@@ -148,7 +148,7 @@ def _forward_block(q_i, k, v, i, blocks, scale, pos, bounds):
     return finalize(state), state
 
 
-def backward_rows(q, k, v, do, q_rows, k_rows, scale: float | None = None, row_chunk: int = 1024):
+def backward_rows(q, k, v, do, q_rows, k_rows, scale: float | None = None, row_chunk: int = 1024, pos=None):
     """Selected rows of (dQ, dK, dV) for one (batch, head) -- [N, d] inputs --
     for checking full-size runs the dense backward cannot hold in memory.
 
@@ -157,7 +157,8 @@ def backward_rows(q, k, v, do, q_rows, k_rows, scale: float | None = None, row_c
     query row, so every row's log-sum-exp L_i and D_i are computed first in a
     streaming pass over ``row_chunk`` query rows at a time (same formulas as
     ``dense_attention_backward``: dV = P^T dO, dS = P * (dP - D),
-    dQ = s dS K, dK = s dS^T Q).
+    dQ = s dS K, dK = s dS^T Q).  With ``pos`` (the position of every row,
+    queries and keys alike) keys after a query's position are masked.
     Returns (dq[len(q_rows), d], dk[len(k_rows), d], dv[len(k_rows), dv])."""
     q, k, v, do = (_as_f64(x) for x in (q, k, v, do))
     if scale is None:
@@ -165,33 +166,46 @@ def backward_rows(q, k, v, do, q_rows, k_rows, scale: float | None = None, row_c
     q_rows = np.asarray(q_rows, dtype=np.int64)
     k_rows = np.asarray(k_rows, dtype=np.int64)
     n = q.shape[0]
-    lse, dd = _lse_and_dd(q, k, v, do, scale, row_chunk)
+    pos = None if pos is None else np.asarray(pos)
+
+    def masked(s, qi, kj_idx):
+        # -inf where the key comes after the query (positions of rows qi, keys kj_idx)
+        if pos is None:
+            return s
+        return np.where(pos[kj_idx][None, :] > pos[qi][:, None], -np.inf, s)
+
+    lse, dd = _lse_and_dd(q, k, v, do, scale, row_chunk, masked)
     kj = k[k_rows]
     dk = np.zeros((len(k_rows), q.shape[1]))
     dv = np.zeros((len(k_rows), v.shape[1]))
     # pass 2: the chosen key rows' dK, dV over every query row
+    all_k = np.arange(k.shape[0])
     for a in range(0, n, row_chunk):
-        p = np.exp((q[a:a + row_chunk] @ kj.T) * scale - lse[a:a + row_chunk, None])
+        qi = np.arange(a, min(a + row_chunk, n))
+        p = np.exp(masked((q[a:a + row_chunk] @ kj.T) * scale, qi, k_rows) - lse[a:a + row_chunk, None])
         dpj = do[a:a + row_chunk] @ v[k_rows].T
         dsj = p * (dpj - dd[a:a + row_chunk, None])
         dv += p.T @ do[a:a + row_chunk]
         dk += scale * dsj.T @ q[a:a + row_chunk]
     # the chosen query rows' dQ
-    s = (q[q_rows] @ k.T) * scale
+    s = masked((q[q_rows] @ k.T) * scale, q_rows, all_k)
     p = np.exp(s - lse[q_rows, None])
     dp = do[q_rows] @ v.T
     dq = scale * (p * (dp - dd[q_rows, None])) @ k
     return dq, dk, dv
 
 
-def _lse_and_dd(q, k, v, do, scale, row_chunk):
+def _lse_and_dd(q, k, v, do, scale, row_chunk, masked=lambda s, qi, kj: s):
     """Pass 1 of ``backward_rows``: every query row's L_i = m_i + log l_i and
-    D_i = dO_i . O_i, ``row_chunk`` rows at a time."""
+    D_i = dO_i . O_i, ``row_chunk`` rows at a time.  (Every row sees at least
+    its own key under a causal mask, so no row is empty.)"""
     n = q.shape[0]
     lse = np.empty(n)
     dd = np.empty(n)
+    all_k = np.arange(k.shape[0])
     for a in range(0, n, row_chunk):
-        s = (q[a:a + row_chunk] @ k.T) * scale
+        qi = np.arange(a, min(a + row_chunk, n))
+        s = masked((q[a:a + row_chunk] @ k.T) * scale, qi, all_k)
         m = s.max(axis=1, keepdims=True)
         e = np.exp(s - m)
         z = e.sum(axis=1, keepdims=True)

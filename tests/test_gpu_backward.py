@@ -209,3 +209,32 @@ def test_ring_backward_128k_sampled(ra):
     idx = torch.from_numpy(rows).cuda()
     for name, g, ww in zip(("dQ", "dK", "dV"), (dq, dk, dv), want):
         check_grad(g[0, 0, idx], ww, "bf16", f"128K {name}")
+
+
+def test_ring_backward_128k_causal_sampled(ra):
+    """The headline shape under the zig-zag causal layout: head 0's dQ, dK, dV
+    on 64 sampled rows against the oracle's streaming row sampler with the
+    rows' positions (one full fp64 pass over head 0)."""
+    import workloads
+    from tests.helpers import sample_rows
+
+    w = workloads.WORKLOADS[3]
+    layout = "zigzag"
+    _say(f"ring backward full size causal {layout} {w.describe()}")
+    q, k, v = workloads.make_inputs(w, device="cuda")
+    do = torch.randn(q.shape, generator=torch.Generator(device="cuda").manual_seed(w.seed + 9),
+                     device="cuda").to(q.dtype)
+    out, lse = ra.ra_ring_forward_ex(q, k, v, w.P, layout)
+    dq, dk, dv = ra.ra_ring_backward(q, k, v, out, do, lse, w.P, layout)
+    torch.cuda.synchronize()
+    for g in (dq, dk, dv):
+        assert torch.isfinite(g).all()
+    rows = sample_rows(w.P, w.b, 4, seed=w.seed + 1)
+    pos = layouts.positions(layout, w.P, w.b).reshape(-1)
+    print(f"[case] oracle pass over head 0 ({len(rows)} query and key rows)", flush=True)
+    want = ob.backward_rows(to64(q[0, 0]), to64(k[0, 0]), to64(v[0, 0]), to64(do[0, 0]), rows, rows,
+                            row_chunk=2048, pos=pos)
+    print("[case] oracle done", flush=True)
+    idx = torch.from_numpy(rows).cuda()
+    for name, g, ww in zip(("dQ", "dK", "dV"), (dq, dk, dv), want):
+        check_grad(g[0, 0, idx], ww, "bf16", f"128K causal {name}")

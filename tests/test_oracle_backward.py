@@ -163,6 +163,27 @@ def test_backward_rows_matches_autograd():
     np.testing.assert_allclose(dk, want[1][rows_k], rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("layout", ["contiguous", "zigzag"])
+def test_backward_rows_causal_matches_autograd(layout):
+    """With positions: equals torch fp64 autograd through the causal attention
+    of the sequence in position order, at the rows' positions."""
+    P, b, d = 4, 40, 8
+    n = P * b
+    pos = layouts.positions(layout, P, b).reshape(-1)
+    q, k, v, do = (_rand((n, d), s, 1.3) for s in (41, 42, 43, 44))
+    # in position order the mask is plain is_causal; row r sits at position pos[r]
+    order = np.argsort(pos)
+    want_sorted = _autograd(q[order], k[order], v[order], do[order], causal=True)
+    want = [np.empty_like(w) for w in want_sorted]
+    for w, ws in zip(want, want_sorted):
+        w[order] = ws
+    rows = np.array([0, 11, 77, n - 1])
+    dq, dk, dv = ob.backward_rows(q, k, v, do, rows, rows, row_chunk=33, pos=pos)
+    np.testing.assert_allclose(dq, want[0][rows], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dk, want[1][rows], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dv, want[2][rows], rtol=0, atol=1e-12)
+
+
 @pytest.mark.parametrize("mistake", ["no_D", "lse_without_log"])
 def test_backward_rows_planted_mistakes_are_caught(monkeypatch, mistake):
     """Mistakes planted in the sampler's first pass fail the autograd comparison."""
@@ -172,7 +193,7 @@ def test_backward_rows_planted_mistakes_are_caught(monkeypatch, mistake):
     want = _autograd(q, k, v, do)
     real = ob._lse_and_dd
 
-    def bad(q_, k_, v_, do_, scale, chunk):
+    def bad(q_, k_, v_, do_, scale, chunk, masked=None):
         lse, dd = real(q_, k_, v_, do_, scale, chunk)
         if mistake == "no_D":
             return lse, np.zeros_like(dd)
