@@ -20,7 +20,10 @@ five products of the backward, 10 d FLOP per (query, key) pair.  With --graph
 the step is captured once into a HIP graph (stream capture: fold launches,
 hand-off copies, side stream and events all become nodes) and the timed steps
 are graph replays; the fold-launch times in `roofline` then come from eager
-steps.  `clock` is the shader clock the driver reported while the timed steps
+steps.  --device-sweep instead times one device's ring step at its real shape
+(one ra_fold_block of a b-row query block with one b-row visiting block, B1 H32
+d128 bf16) for several b, next to the time one K/V block of that size takes
+over one xGMI link, and prints one JSON line with a row per b.  `clock` is the shader clock the driver reported while the timed steps
 ran (sampled from pp_dpm_sclk by a host thread) and the step throughput as a
 share of the peak scaled to that clock (null where the file is not readable).
 """
@@ -206,6 +209,49 @@ class ClockSampler:
                 "peak_at_clock": round(at_clock, 1), "pct_peak_at_clock": round(100.0 * value / at_clock, 2)}
 
 
+XGMI_LINK_GBPS = 153.0  # one MI355X xGMI link, one direction (GB/s)
+
+
+def device_sweep(torch, ra, steps: int, warmup: int) -> int:
+    """One device's share of a ring step: fold one visiting block of b keys into
+    the state of the resident block's b query rows (B1 H32 d128 bf16), timed with
+    HIP events on the launch stream, against the time the next K/V block (2 b d
+    bf16 per head) takes over one xGMI link.  The step hides the hand-off when the
+    fold takes at least as long as the transfer on the links the ring uses."""
+    B, H, d = 1, 32, 128
+    rows = []
+    for b in (1024, 2048, 4096, 8192, 16384, 32768):
+        g = torch.Generator(device="cuda").manual_seed(5000 + b)
+        q, k, v = (torch.randn((B, H, b, d), generator=g, device="cuda").to(torch.bfloat16) for _ in range(3))
+        m = torch.empty((B, H, b), device="cuda")
+        l = torch.empty_like(m)
+        o = torch.empty((B, H, b, d), device="cuda")
+        ra.ra_state_init(m, l, o)
+        n = max(steps, 10) if b >= 8192 else max(steps, 50)
+        for _ in range(max(warmup, 3)):
+            ra.ra_fold_block(q, k, v, m, l, o)
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(n):
+            ra.ra_fold_block(q, k, v, m, l, o)
+        end.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / n
+        flops = 4.0 * B * H * b * b * d
+        kv_bytes = 2.0 * B * H * b * d * 2
+        xfer_ms = kv_bytes / (XGMI_LINK_GBPS * 1e9) * 1e3
+        row = {"b": b, "fold_ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+               "kv_block_mb": round(kv_bytes / 1e6, 2), "xgmi_1link_ms": round(xfer_ms, 4),
+               "links_needed": round(xfer_ms / ms, 2)}
+        print(f"[bench] device sweep {row}", file=sys.stderr, flush=True)
+        rows.append(row)
+        del q, k, v, m, l, o
+    print(json.dumps({"mode": "device-sweep", "shape": {"B": B, "H": H, "d": d, "dtype": "bf16"},
+                      "xgmi_link_gbps": XGMI_LINK_GBPS, "rows": rows}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -219,6 +265,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--graph", action="store_true",
                     help="capture one step into a HIP graph (stream capture) and time its replays")
+    ap.add_argument("--device-sweep", action="store_true",
+                    help="time one device's fold step for several block sizes b against one block's xGMI transfer")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 1 GiB device copy (a known-size reference for HBM byte counters)")
     args = ap.parse_args()
@@ -239,6 +287,8 @@ def main() -> int:
         return 1
     torch.cuda.set_device(0)
     ra.load()
+    if args.device_sweep:
+        return device_sweep(torch, ra, args.steps, args.warmup)
     w = workloads.WORKLOADS[args.workload]
     print(f"[bench] workload {w.describe()} steps={args.steps} warmup={args.warmup}", file=sys.stderr, flush=True)
     q, k, v = workloads.make_inputs(w, device="cuda")
