@@ -217,7 +217,9 @@ def device_sweep(torch, ra, steps: int, warmup: int) -> int:
     the state of the resident block's b query rows (B1 H32 d128 bf16), timed with
     HIP events on the launch stream, against the time the next K/V block (2 b d
     bf16 per head) takes over one xGMI link.  The step hides the hand-off when the
-    fold takes at least as long as the transfer on the links the ring uses."""
+    fold takes at least as long as the transfer on the links the ring uses.  The
+    same fold run as a one-device ring (no state loaded or stored) gives the share
+    of the step the state spill costs."""
     B, H, d = 1, 32, 128
     rows = []
     for b in (1024, 2048, 4096, 8192, 16384, 32768):
@@ -227,26 +229,35 @@ def device_sweep(torch, ra, steps: int, warmup: int) -> int:
         l = torch.empty_like(m)
         o = torch.empty((B, H, b, d), device="cuda")
         ra.ra_state_init(m, l, o)
+        out = torch.empty_like(q)
+        ws = torch.empty(ra.ra_ring_workspace_bytes(q.dtype, B, H, b, d, 1, 1), dtype=torch.uint8, device="cuda")
         n = max(steps, 10) if b >= 8192 else max(steps, 50)
-        for _ in range(max(warmup, 3)):
-            ra.ra_fold_block(q, k, v, m, l, o)
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        start.record()
-        for _ in range(n):
-            ra.ra_fold_block(q, k, v, m, l, o)
-        end.record()
-        torch.cuda.synchronize()
-        ms = start.elapsed_time(end) / n
+
+        def timed(fn):
+            for _ in range(max(warmup, 3)):
+                fn()
+            start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            start.record()
+            for _ in range(n):
+                fn()
+            end.record()
+            torch.cuda.synchronize()
+            return start.elapsed_time(end) / n
+
+        ms = timed(lambda: ra.ra_fold_block(q, k, v, m, l, o))
+        # the same fold as a one-device ring: no state loaded or stored, O written directly
+        ms_nospill = timed(lambda: ra.ra_ring_forward(q, k, v, 1, out=out, workspace=ws))
         flops = 4.0 * B * H * b * b * d
         kv_bytes = 2.0 * B * H * b * d * 2
         xfer_ms = kv_bytes / (XGMI_LINK_GBPS * 1e9) * 1e3
         row = {"b": b, "fold_ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+               "fold_no_spill_ms": round(ms_nospill, 4), "spill_share": round(1.0 - ms_nospill / ms, 4),
                "kv_block_mb": round(kv_bytes / 1e6, 2), "xgmi_1link_ms": round(xfer_ms, 4),
                "links_needed": round(xfer_ms / ms, 2)}
         print(f"[bench] device sweep {row}", file=sys.stderr, flush=True)
         rows.append(row)
-        del q, k, v, m, l, o
+        del q, k, v, m, l, o, out, ws
     print(json.dumps({"mode": "device-sweep", "shape": {"B": B, "H": H, "d": d, "dtype": "bf16"},
                       "xgmi_link_gbps": XGMI_LINK_GBPS, "rows": rows}), flush=True)
     return 0
