@@ -127,13 +127,43 @@ ra_status_t get_dev(DevRes** out) {
     return RA_OK;
   }
   DevRes* r = new DevRes;
-  RA_HIP(hipStreamCreateWithFlags(&r->side, hipStreamNonBlocking), "hipStreamCreateWithFlags");
   hipEvent_t* evs[6] = {&r->fork, &r->join, &r->ready[0], &r->ready[1], &r->freed[0], &r->freed[1]};
-  for (hipEvent_t* e : evs) RA_HIP(hipEventCreateWithFlags(e, hipEventDisableTiming), "hipEventCreateWithFlags");
+  // On a failure part-way, release what was created and leave no entry, so a
+  // later call tries again.
+  auto undo = [&](hipError_t e, const char* what) {
+    for (hipEvent_t* ev : evs)
+      if (*ev != nullptr) (void)hipEventDestroy(*ev);
+    if (r->side != nullptr) (void)hipStreamDestroy(r->side);
+    delete r;
+    return hip_fail(e, what);
+  };
+  hipError_t e = hipStreamCreateWithFlags(&r->side, hipStreamNonBlocking);
+  if (e != hipSuccess) return undo(e, "hipStreamCreateWithFlags");
+  for (hipEvent_t* ev : evs) {
+    e = hipEventCreateWithFlags(ev, hipEventDisableTiming);
+    if (e != hipSuccess) return undo(e, "hipEventCreateWithFlags");
+  }
   g_dev[dev] = r;
   *out = r;
   return RA_OK;
 }
+
+// Undoes a ring driver's set-up when it returns early on an error: the side
+// stream is joined back into the caller's stream (so no hand-off copy still
+// reads K or V after the call has returned) and a workspace the library
+// allocated is freed.  The success path does both itself, checking each
+// call, after clearing the fields.  Errors here are not reported: the call
+// already returns the first one.
+struct RingCleanup {
+  hipStream_t stream = nullptr;
+  hipStream_t side = nullptr;  // set while the side stream is forked
+  hipEvent_t join = nullptr;
+  void* ws = nullptr;  // set while an internally allocated workspace is live
+  ~RingCleanup() {
+    if (side != nullptr && hipEventRecord(join, side) == hipSuccess) (void)hipStreamWaitEvent(stream, join, 0);
+    if (ws != nullptr) (void)hipFreeAsync(ws, stream);
+  }
+};
 
 constexpr size_t kAlign = 256;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -470,10 +500,15 @@ ra_status_t ring_forward_impl(const void* q, const int64_t q_strides[3], const v
   DevRes* dr = nullptr;
   if ((st = get_dev(&dr)) != RA_OK) return st;
   std::lock_guard<std::mutex> guard(dr->mu);
+  RingCleanup cleanup;  // after the lock: runs while the device's resources are still held
+  cleanup.stream = stream;
 
   void* ws = workspace;
   const bool own_ws = ws == nullptr;
-  if (own_ws) RA_HIP(hipMallocAsync(&ws, L.total, stream), "hipMallocAsync (ring workspace)");
+  if (own_ws) {
+    RA_HIP(hipMallocAsync(&ws, L.total, stream), "hipMallocAsync (ring workspace)");
+    cleanup.ws = ws;
+  }
   char* base = (char*)ws;
   float* m = (float*)(base + L.off_m);
   float* l = (float*)(base + L.off_l);
@@ -488,6 +523,8 @@ ra_status_t ring_forward_impl(const void* q, const int64_t q_strides[3], const v
   if (!serial) {
     RA_HIP(hipEventRecord(dr->fork, stream), "hipEventRecord");
     RA_HIP(hipStreamWaitEvent(side, dr->fork, 0), "hipStreamWaitEvent");
+    cleanup.side = side;
+    cleanup.join = dr->join;
   }
   // Data for step t >= 1 lives in slot (t - 1) % 2.
   auto slot_of = [](int t) { return (t - 1) & 1; };
@@ -570,8 +607,12 @@ ra_status_t ring_forward_impl(const void* q, const int64_t q_strides[3], const v
   if (!serial) {
     RA_HIP(hipEventRecord(dr->join, side), "hipEventRecord");
     RA_HIP(hipStreamWaitEvent(stream, dr->join, 0), "hipStreamWaitEvent");
+    cleanup.side = nullptr;
   }
-  if (own_ws) RA_HIP(hipFreeAsync(ws, stream), "hipFreeAsync (ring workspace)");
+  if (own_ws) {
+    cleanup.ws = nullptr;
+    RA_HIP(hipFreeAsync(ws, stream), "hipFreeAsync (ring workspace)");
+  }
   return RA_OK;
 }
 
@@ -693,9 +734,14 @@ RA_API ra_status_t ra_ring_backward(const void* q, const int64_t q_strides[3], c
   const size_t es = esize(dt);
   const bool bf16 = dt == RA_DTYPE_BF16;
 
+  RingCleanup cleanup;
+  cleanup.stream = stream;
   void* ws = workspace;
   const bool own_ws = ws == nullptr;
-  if (own_ws) RA_HIP(hipMallocAsync(&ws, L.total, stream), "hipMallocAsync (backward workspace)");
+  if (own_ws) {
+    RA_HIP(hipMallocAsync(&ws, L.total, stream), "hipMallocAsync (backward workspace)");
+    cleanup.ws = ws;
+  }
   char* base = (char*)ws;
   float* nl2 = (float*)(base + L.off_nl2);
   float* dd = (float*)(base + L.off_dd);
@@ -767,7 +813,10 @@ RA_API ra_status_t ra_ring_backward(const void* q, const int64_t q_strides[3], c
   RA_HIP(ra::launch_scale_cast(dv_acc, 1.0f, dv, dv_strides[0], dv_strides[1], dv_strides[2], bf16, (int)B, (int)H, N,
                                (int)d, stream),
          "dV cast launch");
-  if (own_ws) RA_HIP(hipFreeAsync(ws, stream), "hipFreeAsync (backward workspace)");
+  if (own_ws) {
+    cleanup.ws = nullptr;
+    RA_HIP(hipFreeAsync(ws, stream), "hipFreeAsync (backward workspace)");
+  }
   return RA_OK;
 }
 
