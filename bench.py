@@ -44,27 +44,87 @@ if ROOT not in sys.path:
 METRIC = "ring-fold attention TFLOP/s and % MFMA bf16 peak, 128K tokens P=16, 1 GPU"
 PEAK = {"bf16": 2500.0, "f32": 157.3}  # MI355X published dense TFLOP/s: bf16 MFMA, fp32 vector
 FOLD_SOURCES = {"bf16": "fold_bf16.hip", "f32": "fold_f32.hip"}
+BWD_SOURCES = {"bf16": "fold_bwd_bf16.hip", "f32": "fold_bwd_f32.hip"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fold_traffic.json")
 
 
-def _source_hash(dtype: str) -> str:
-    path = os.path.join(ROOT, "blockwise_online_softmax_fold_amd", "csrc", FOLD_SOURCES[dtype])
+def _source_hash(dtype: str, backward: bool = False) -> str:
+    name = BWD_SOURCES[dtype] if backward else FOLD_SOURCES[dtype]
+    path = os.path.join(ROOT, "blockwise_online_softmax_fold_amd", "csrc", name)
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def _traffic(workload: str, dtype: str):
-    """HBM bytes per fold launch from the committed rocprofv3 counter summary,
-    only if it was taken on the current kernel source."""
+def _traffic_key(workload: str, backward: bool) -> str:
+    return workload + ("/backward" if backward else "")
+
+
+def _traffic(workload: str, dtype: str, backward: bool = False):
+    """HBM bytes per launch (a fold launch, or one backward step's dQ + dK/dV
+    launch pair) from the committed rocprofv3 counter summary, only if it was
+    taken on the current kernel source."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    ent = rec.get(workload)
-    if not ent or ent.get("source_sha256_16") != _source_hash(dtype):
+    ent = rec.get(_traffic_key(workload, backward))
+    if not ent or ent.get("source_sha256_16") != _source_hash(dtype, backward):
         return None
     return ent.get("hbm_bytes_per_launch")
+
+
+def traffic_from(fetch_dir: str, write_dir: str, workload: str, dtype: str, backward: bool) -> int:
+    """Turn two rocprofv3 --pmc runs of `bench.py --copy-calibration` (one with
+    FETCH_SIZE, one with WRITE_SIZE; KiB per dispatch) into HBM bytes per launch
+    and record them in the traffic file under the current kernel source's hash.
+    Each counter is scaled by what it read for a transfer of known size: the
+    1 GiB device copy for FETCH_SIZE, the 1 GiB fill before it for WRITE_SIZE."""
+    import glob
+    import sqlite3
+
+    def rows(d: str, counter: str):
+        dbs = glob.glob(os.path.join(d, "**", "*_results.db"), recursive=True)
+        if len(dbs) != 1:
+            raise SystemExit(f"expected one *_results.db under {d}, found {len(dbs)}")
+        with sqlite3.connect(dbs[0]) as db:
+            return list(db.execute("select dispatch_id, kernel_name, value from counters_collection "
+                                   "where counter_name = ? order by dispatch_id", (counter,)))
+
+    f, w = rows(fetch_dir, "FETCH_SIZE"), rows(write_dir, "WRITE_SIZE")
+    gib = float(1 << 30)
+    plain_copy = lambda n: n.startswith("__amd_rocclr_copyBuffer") and "Rect" not in n  # noqa: E731
+    # the calibration copy is the largest plain device copy of the run; the fill
+    # that wrote its 1 GiB source is the last fill dispatched before it
+    cal_f = max(v for _, name, v in f if plain_copy(name))
+    copy_id = max(((v, i) for i, name, v in w if plain_copy(name)))[1]
+    fills = [(i, v) for i, name, v in w if i < copy_id and "Fill" in name]
+    if not fills:
+        raise SystemExit("no fill dispatch before the calibration copy: run bench.py with --copy-calibration")
+    cal_w = max(fills)[1]
+    kf, kw = gib / (cal_f * 1024), gib / (cal_w * 1024)
+    pick = (lambda n: "bwd_dq_kernel" in n or "bwd_dkdv_kernel" in n) if backward else (lambda n: "fold_" in n)
+    fb = [v * 1024 * kf for _, name, v in f if pick(name)]
+    wb = [v * 1024 * kw for _, name, v in w if pick(name)]
+    per = 2 if backward else 1  # a backward "launch" is the dQ + dK/dV pair of one ring step
+    if not fb or len(fb) != len(wb) or len(fb) % per:
+        raise SystemExit(f"unexpected dispatch counts: {len(fb)} fetch, {len(wb)} write")
+    n = len(fb) // per
+    ent = {"read_scale": kf, "write_scale": kw, "launches": n,
+           "read_bytes_per_launch": sum(fb) / n, "write_bytes_per_launch": sum(wb) / n}
+    ent["hbm_bytes_per_launch"] = ent["read_bytes_per_launch"] + ent["write_bytes_per_launch"]
+    ent["source_sha256_16"] = _source_hash(dtype, backward)
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        rec = {}
+    rec[_traffic_key(workload, backward)] = ent
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps({_traffic_key(workload, backward): ent}, indent=1))
+    return 0
 
 
 def _positions(layout: str, P: int, b: int):
@@ -280,7 +340,16 @@ def main() -> int:
                     help="time one device's fold step for several block sizes b against one block's xGMI transfer")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 1 GiB device copy (a known-size reference for HBM byte counters)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU: record HBM bytes per launch of the selected workload and pass from two "
+                         "rocprofv3 --pmc output folders (FETCH_SIZE, WRITE_SIZE) of --copy-calibration runs")
     args = ap.parse_args()
+    if args.traffic_from:
+        sys.path.insert(0, ROOT)
+        import workloads
+
+        w = workloads.WORKLOADS[args.workload]
+        return traffic_from(*args.traffic_from, w.name, w.dtype, args.backward)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -388,7 +457,7 @@ def main() -> int:
         "peak": peak,
         "unit": "TFLOP/s",
         "frac": round(achieved / peak, 4),
-        "traffic": None if args.backward else _traffic(w.name, w.dtype),
+        "traffic": None if args.causal else _traffic(w.name, w.dtype, args.backward),
         "kernel": (f"bwd_dq_kernel<{w.d}> + bwd_dkdv_kernel<{w.d}> (one step)" if args.backward
                    else f"fold_{w.dtype}_kernel<{w.d}>"),
         "flop_per_launch": flops_per_launch,
