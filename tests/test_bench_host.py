@@ -1,0 +1,90 @@
+"""Host-side logic of bench.py that needs no GPU: the refusal of more than one
+GPU and the derivation of HBM bytes per launch from rocprofv3 counter databases."""
+
+from __future__ import annotations
+
+import json
+import os
+import sqlite3
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+GIB_KIB = 1 << 20
+
+
+def _db(folder, counter: str, dispatches):
+    os.makedirs(folder, exist_ok=True)
+    with sqlite3.connect(os.path.join(folder, "run_results.db")) as db:
+        db.execute("create table counters_collection (dispatch_id int, kernel_name text, counter_name text, value real)")
+        db.executemany("insert into counters_collection values (?, ?, ?, ?)",
+                       [(i, name, counter, v) for i, (name, v) in enumerate(dispatches, 1)])
+
+
+def _run(tmp_path, monkeypatch, fetch, write, backward):
+    fd, wd = str(tmp_path / "f"), str(tmp_path / "w")
+    _db(fd, "FETCH_SIZE", fetch)
+    _db(wd, "WRITE_SIZE", write)
+    out = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(out))
+    assert bench.traffic_from(fd, wd, "ring-128k-P16", "bf16", backward) == 0
+    return json.loads(out.read_text())
+
+
+def test_forward_traffic_scaled_by_the_calibration(tmp_path, monkeypatch):
+    # the fetch counter reads half the bytes of the 1 GiB copy: every fetch is scaled by 2
+    fetch = [("FillFunctor<float>", 10.0), ("__amd_rocclr_copyBuffer", GIB_KIB / 2),
+             ("fold_bf16_kernel<128, 8>", 1000.0), ("fold_bf16_kernel<128, 8>", 3000.0),
+             ("__amd_rocclr_copyBufferRectAligned", 9 * GIB_KIB)]
+    write = [("FillFunctor<float>", GIB_KIB), ("__amd_rocclr_copyBuffer", GIB_KIB),
+             ("fold_bf16_kernel<128, 8>", 500.0), ("fold_bf16_kernel<128, 8>", 700.0),
+             ("__amd_rocclr_copyBufferRectAligned", 9 * GIB_KIB)]
+    rec = _run(tmp_path, monkeypatch, fetch, write, backward=False)["ring-128k-P16"]
+    assert rec["launches"] == 2
+    assert rec["read_scale"] == pytest.approx(2.0) and rec["write_scale"] == pytest.approx(1.0)
+    assert rec["read_bytes_per_launch"] == pytest.approx(2000.0 * 1024 * 2)
+    assert rec["write_bytes_per_launch"] == pytest.approx(600.0 * 1024)
+    assert rec["hbm_bytes_per_launch"] == pytest.approx(rec["read_bytes_per_launch"] + rec["write_bytes_per_launch"])
+    assert rec["source_sha256_16"] == bench._source_hash("bf16")
+
+
+def test_write_scale_comes_from_the_fill_before_the_copy(tmp_path, monkeypatch):
+    # a larger elementwise write (a 2 GiB random fill) and a later fill must not be taken
+    # for the calibration: only the last fill before the calibration copy counts
+    fetch = [("distribution_elementwise", 5.0), ("FillFunctor<float>", 1.0),
+             ("__amd_rocclr_copyBuffer", GIB_KIB / 2), ("bwd_dq_kernel<128, 8>", 100.0),
+             ("bwd_dkdv_kernel<128, 8>", 300.0), ("FillFunctor<float>", 1.0)]
+    write = [("distribution_elementwise", 2 * GIB_KIB), ("FillFunctor<float>", GIB_KIB),
+             ("__amd_rocclr_copyBuffer", GIB_KIB), ("bwd_dq_kernel<128, 8>", 40.0),
+             ("bwd_dkdv_kernel<128, 8>", 60.0), ("FillFunctor<float>", 4 * GIB_KIB)]
+    rec = _run(tmp_path, monkeypatch, fetch, write, backward=True)["ring-128k-P16/backward"]
+    assert rec["write_scale"] == pytest.approx(1.0)
+    assert rec["launches"] == 1  # one dQ + dK/dV pair
+    assert rec["read_bytes_per_launch"] == pytest.approx(400.0 * 1024 * 2)
+    assert rec["write_bytes_per_launch"] == pytest.approx(100.0 * 1024)
+    assert rec["source_sha256_16"] == bench._source_hash("bf16", backward=True)
+
+
+def test_traffic_is_dropped_when_the_source_changes(tmp_path, monkeypatch):
+    out = tmp_path / "traffic.json"
+    out.write_text(json.dumps({"ring-128k-P16": {"hbm_bytes_per_launch": 7.0, "source_sha256_16": "0" * 16}}))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(out))
+    assert bench._traffic("ring-128k-P16", "bf16") is None
+    out.write_text(json.dumps({"ring-128k-P16": {"hbm_bytes_per_launch": 7.0,
+                                                 "source_sha256_16": bench._source_hash("bf16")}}))
+    assert bench._traffic("ring-128k-P16", "bf16") == 7.0
+    assert bench._traffic("ring-128k-P16", "bf16", backward=True) is None
+
+
+def test_more_than_one_gpu_is_refused():
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr
+    assert res.stdout == ""
