@@ -40,6 +40,17 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
+// max / sum of a value over the four lanes l, l ^ 16, l ^ 32, l ^ 48
+// (v_permlane16_swap pairs rows 0-1 and 2-3 of 16 lanes, then the 32-lane swap).
+__device__ __forceinline__ float quad_max(float x) {
+  auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return pair_max(fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])));
+}
+__device__ __forceinline__ float quad_sum(float x) {
+  auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return pair_sum(__uint_as_float(sw[0]) + __uint_as_float(sw[1]));
+}
+
 __device__ __forceinline__ unsigned pack_bf16(float a, float b) {
   bf16x2 v = {(__bf16)a, (__bf16)b};
   return __builtin_bit_cast(unsigned, v);

@@ -411,8 +411,7 @@ hipError_t launch_fold_bf16(const FoldParams& p, int d, hipStream_t s) {
       fold_bf16_kernel<128, waves_for(128)><<<gd, bd, 0, s>>>(p);
       break;
     case 256:
-      fold_bf16_kernel<256, waves_for(256)><<<gd, bd, 0, s>>>(p);
-      break;
+      return launch_fold_bf16_r16(p, d, s);
     default:
       return hipErrorInvalidValue;
   }
