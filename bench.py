@@ -43,13 +43,17 @@ if ROOT not in sys.path:
 
 METRIC = "ring-fold attention TFLOP/s and % MFMA bf16 peak, 128K tokens P=16, 1 GPU"
 PEAK = {"bf16": 2500.0, "f32": 157.3}  # MI355X published dense TFLOP/s: bf16 MFMA, fp32 vector
-FOLD_SOURCES = {"bf16": "fold_bf16.hip", "f32": "fold_f32.hip"}
+FOLD_SOURCES = {"bf16": "fold_bf16.hip", "f32": "fold_f32.hip", "bf16/d256": "fold_bf16_r16.hip"}
 BWD_SOURCES = {"bf16": "fold_bwd_bf16.hip", "f32": "fold_bwd_f32.hip"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fold_traffic.json")
 
 
-def _source_hash(dtype: str, backward: bool = False) -> str:
-    name = BWD_SOURCES[dtype] if backward else FOLD_SOURCES[dtype]
+def _source_hash(dtype: str, backward: bool = False, d: int = 128) -> str:
+    """Hash of the source file that holds the kernel of this dtype, head dim and pass."""
+    if backward:
+        name = BWD_SOURCES[dtype]
+    else:
+        name = FOLD_SOURCES.get(f"{dtype}/d{d}", FOLD_SOURCES[dtype])
     path = os.path.join(ROOT, "blockwise_online_softmax_fold_amd", "csrc", name)
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -59,7 +63,7 @@ def _traffic_key(workload: str, backward: bool) -> str:
     return workload + ("/backward" if backward else "")
 
 
-def _traffic(workload: str, dtype: str, backward: bool = False):
+def _traffic(workload: str, dtype: str, backward: bool = False, d: int = 128):
     """HBM bytes per launch (a fold launch, or one backward step's dQ + dK/dV
     launch pair) from the committed rocprofv3 counter summary, only if it was
     taken on the current kernel source."""
@@ -69,12 +73,12 @@ def _traffic(workload: str, dtype: str, backward: bool = False):
     except (OSError, ValueError):
         return None
     ent = rec.get(_traffic_key(workload, backward))
-    if not ent or ent.get("source_sha256_16") != _source_hash(dtype, backward):
+    if not ent or ent.get("source_sha256_16") != _source_hash(dtype, backward, d):
         return None
     return ent.get("hbm_bytes_per_launch")
 
 
-def traffic_from(fetch_dir: str, write_dir: str, workload: str, dtype: str, backward: bool) -> int:
+def traffic_from(fetch_dir: str, write_dir: str, workload: str, dtype: str, backward: bool, d: int = 128) -> int:
     """Turn two rocprofv3 --pmc runs of `bench.py --copy-calibration` (one with
     FETCH_SIZE, one with WRITE_SIZE; KiB per dispatch) into HBM bytes per launch
     and record them in the traffic file under the current kernel source's hash.
@@ -113,7 +117,7 @@ def traffic_from(fetch_dir: str, write_dir: str, workload: str, dtype: str, back
     ent = {"read_scale": kf, "write_scale": kw, "launches": n,
            "read_bytes_per_launch": sum(fb) / n, "write_bytes_per_launch": sum(wb) / n}
     ent["hbm_bytes_per_launch"] = ent["read_bytes_per_launch"] + ent["write_bytes_per_launch"]
-    ent["source_sha256_16"] = _source_hash(dtype, backward)
+    ent["source_sha256_16"] = _source_hash(dtype, backward, d)
     try:
         with open(TRAFFIC_FILE) as fh:
             rec = json.load(fh)
@@ -349,7 +353,7 @@ def main() -> int:
         import workloads
 
         w = workloads.WORKLOADS[args.workload]
-        return traffic_from(*args.traffic_from, w.name, w.dtype, args.backward)
+        return traffic_from(*args.traffic_from, w.name, w.dtype, args.backward, w.d)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -457,8 +461,9 @@ def main() -> int:
         "peak": peak,
         "unit": "TFLOP/s",
         "frac": round(achieved / peak, 4),
-        "traffic": None if args.causal else _traffic(w.name, w.dtype, args.backward),
+        "traffic": None if args.causal else _traffic(w.name, w.dtype, args.backward, w.d),
         "kernel": (f"bwd_dq_kernel<{w.d}> + bwd_dkdv_kernel<{w.d}> (one step)" if args.backward
+                   else f"fold_bf16_r16_kernel<{w.d}>" if (w.dtype, w.d) == ("bf16", 256)
                    else f"fold_{w.dtype}_kernel<{w.d}>"),
         "flop_per_launch": flops_per_launch,
         "avg_launch_ms": round(fold_avg_ms, 4),

@@ -7,7 +7,9 @@
 // l' = alpha l + sum exp(s - m'), o' = alpha o + sum exp(s - m') v.
 //
 // Mapping onto CDNA4:
-//  * A workgroup is NW waves (8 for d = 128, 4 for d = 64 and 256); each wave
+//  * d = 64 and 128 (d = 256 runs the 16-row kernel of fold_bf16_r16.hip,
+//    whose state fits two waves per SIMD).
+//  * A workgroup is NW waves (8 for d = 128, 4 for d = 64); each wave
 //    owns 32 query rows, so a workgroup owns a 32 NW-row query tile, and every
 //    K/V tile brought into LDS (and through L2) serves all of them.  With 8
 //    waves one workgroup fills a CU at two waves per SIMD.  Q stays in
@@ -15,8 +17,8 @@
 //    loaded once, kept in registers while the visiting block streams past, and
 //    stored once (or normalised and written as the output on the last ring
 //    step).
-//  * The visiting block streams through two LDS buffers in 64-key tiles (32 for
-//    d = 256): K and V row-major, the 16-byte units of each row XOR-swizzled so
+//  * The visiting block streams through two LDS buffers in 64-key tiles: K and
+//    V row-major, the 16-byte units of each row XOR-swizzled so
 //    both read patterns below are free of bank conflicts, filled straight from
 //    global memory by buffer_load ... lds while the other buffer is in use.
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
@@ -59,11 +61,8 @@ using namespace dev;
 // Lazy rescaling threshold (base-2 units): weights stay below 2^kLazy.
 constexpr float kLazy = 8.0f;
 
-// Keys per LDS tile for each head dim.
-template <int D>
-struct TileCfg {
-  static constexpr int TK = D >= 256 ? 32 : 64;
-};
+// Keys per LDS tile.
+constexpr int kTileKeys = 64;
 
 // ---------------------------------------------------------------------------
 // Per tile: wait for it, request the next one into the other buffer, scores,
@@ -72,10 +71,10 @@ struct TileCfg {
 // ragged last tile runs once after it, with key masking.  The per-wave state
 // is written for G groups of 32 query rows; one group per wave is used.
 template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1 : 2)))
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void fold_bf16_kernel(const FoldParams p) {
   constexpr int G = 1;  // query groups of 32 rows per wave
-  constexpr int TK = TileCfg<D>::TK;
+  constexpr int TK = kTileKeys;
   constexpr int NKB = TK / 32;
   constexpr int NC = D / 16;
   constexpr int NDB = D / 32;
@@ -397,6 +396,7 @@ void fold_bf16_kernel(const FoldParams p) {
 constexpr int waves_for(int d) { return d == 128 ? 8 : 4; }
 
 hipError_t launch_fold_bf16(const FoldParams& p, int d, hipStream_t s) {
+  if (d == 256) return launch_fold_bf16_r16(p, d, s);
   const int rows_per_wg = waves_for(d) * 32;
   const int64_t tiles_q = (p.q_rows + rows_per_wg - 1) / rows_per_wg;
   const int64_t grid = tiles_q * p.n_res * p.H * p.B;
@@ -410,8 +410,6 @@ hipError_t launch_fold_bf16(const FoldParams& p, int d, hipStream_t s) {
     case 128:
       fold_bf16_kernel<128, waves_for(128)><<<gd, bd, 0, s>>>(p);
       break;
-    case 256:
-      return launch_fold_bf16_r16(p, d, s);
     default:
       return hipErrorInvalidValue;
   }
