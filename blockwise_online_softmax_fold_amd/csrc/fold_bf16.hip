@@ -63,6 +63,8 @@ constexpr float kLazy = 8.0f;
 
 // Keys per LDS tile.
 constexpr int kTileKeys = 64;
+// Matrix products by which an LDS operand read runs ahead of its use.
+constexpr int kReadAhead = 2;
 
 // ---------------------------------------------------------------------------
 // Per tile: wait for it, request the next one into the other buffer, scores,
@@ -233,19 +235,28 @@ void fold_bf16_kernel(const FoldParams p) {
   }
 
   // S^T of group g against the K tile at kl; the 32-key blocks are
-  // independent accumulation chains, interleaved.
+  // independent accumulation chains, interleaved.  The products are issued in
+  // a fixed order (a scheduling barrier after each), each K operand read
+  // kReadAhead products before its use; left to itself the compiler reads
+  // operands earlier and holds more registers, which measured slower.
   auto scores = [&](f32x16 (&s)[NKB], const __bf16* kl, int g) {
+    constexpr int N = NC * NKB;
+    auto rd = [&](int i) {  // product i: d chunk i / NKB, key block i % NKB
+      return *(const bf16x8*)(kl + 32 * (i % NKB) * D + k_rd[i / NKB]);
+    };
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[kb][i] = 0.0f;
+    bf16x8 a[kReadAhead];
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
+    for (int i = 0; i < kReadAhead; ++i) a[i] = rd(i);
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const bf16x8 a = *(const bf16x8*)(kl + 32 * kb * D + k_rd[c]);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[g][c], s[kb], 0, 0, 0);
-      }
+    for (int i = 0; i < N; ++i) {
+      s[i % NKB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i % kReadAhead], qf[g][i / NKB], s[i % NKB], 0, 0, 0);
+      if (i + kReadAhead < N) a[i % kReadAhead] = rd(i + kReadAhead);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
   // Keys past this row's last visible key (the block's end, or the causal
   // boundary) score -inf.
@@ -299,24 +310,31 @@ void fold_bf16_kernel(const FoldParams p) {
       }
     lpart[g] += lsum;
   };
+  // O^T += V^T P^T over the tile, 16 keys per product, in the same fixed
+  // order with each V^T operand (two transposed reads) read ahead.
   auto values = [&](const unsigned (&pk)[NKB][8], const __bf16* vl, int g) {
+    constexpr int N = NKB * 2 * NDB;
+    bf16x8 b[NKB * 2];  // weights of keys 16 h .. 16 h + 15 of the tile
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int h = 0; h < NKB * 2; ++h) {
+      const int kb = h / 2, c = h % 2;
+      b[h] = __builtin_bit_cast(bf16x8, u32x4{pk[kb][4 * c], pk[kb][4 * c + 1], pk[kb][4 * c + 2], pk[kb][4 * c + 3]});
+    }
+    auto rd = [&](int i) {  // product i: key run pair i / NDB, d block i % NDB
+      const __bf16* vrow = vl + 16 * (i / NDB) * D;
+      const u32x2 w0 = __builtin_bit_cast(u32x2, lds_tr16(vrow + v_rd[0][i % NDB]));
+      const u32x2 w1 = __builtin_bit_cast(u32x2, lds_tr16(vrow + v_rd[1][i % NDB]));
+      return __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w1[0], w1[1]});
+    };
+    bf16x8 a[kReadAhead];
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const u32x4 bw = {pk[kb][4 * c], pk[kb][4 * c + 1], pk[kb][4 * c + 2], pk[kb][4 * c + 3]};
-        const bf16x8 b = __builtin_bit_cast(bf16x8, bw);
-        const __bf16* vrow = vl + (32 * kb + 16 * c) * D;
+    for (int i = 0; i < kReadAhead; ++i) a[i] = rd(i);
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const s16x4 t0 = lds_tr16(vrow + v_rd[0][db]);
-          const s16x4 t1 = lds_tr16(vrow + v_rd[1][db]);
-          const u32x2 w0 = __builtin_bit_cast(u32x2, t0);
-          const u32x2 w1 = __builtin_bit_cast(u32x2, t1);
-          const u32x4 aw = {w0[0], w0[1], w1[0], w1[1]};
-          oacc[g][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, aw), b, oacc[g][db], 0, 0, 0);
-        }
-      }
+    for (int i = 0; i < N; ++i) {
+      oacc[g][i % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i % kReadAhead], b[i / NDB], oacc[g][i % NDB], 0, 0, 0);
+      if (i + kReadAhead < N) a[i % kReadAhead] = rd(i + kReadAhead);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
   // One tile whose K/V sit in LDS buffer `buf`; `masked` applies lim.
