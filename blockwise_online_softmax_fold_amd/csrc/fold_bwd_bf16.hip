@@ -51,6 +51,10 @@ __device__ __forceinline__ int pos_of(const BwdParams& p, int blk_id, int row) {
 // Per-lane byte offsets for the direct loads of one [rows][D] LDS tile of
 // CPW 1 KB chunks per wave: chunk c covers LDS units [64c, 64c + 64); lane i
 // writes unit 64c + i = (row, pos) and fetches global unit pos ^ swz(row).
+// Matrix products by which an LDS operand read runs ahead of its use (the
+// products of each phase are issued in a fixed order).
+constexpr int kReadAhead = 3;
+
 template <int D, int CPW>
 __device__ __forceinline__ void tile_offsets(int wave, int lane, int row_stride, int (&off)[CPW]) {
   constexpr int UPR = D / 8;
@@ -226,10 +230,22 @@ void bwd_dq_kernel(const BwdParams p) {
     const __bf16* kl = lds + buf * 2 * TE;
     const __bf16* vl = kl + TE;
     f32x16 s = {}, dp = {};
+    {  // S^T and dP^T chains interleaved; product i reads its K (even i) or V
+       // (odd i) operand kReadAhead products ahead, in a fixed order
+      constexpr int N = 2 * NC;
+      auto rd = [&](int i) { return *(const bf16x8*)((i % 2 ? vl : kl) + row_rd[i / 2]); };
+      bf16x8 a[kReadAhead];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(kl + row_rd[c]), qf[c], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(vl + row_rd[c]), df[c], dp, 0, 0, 0);
+      for (int i = 0; i < kReadAhead; ++i) a[i] = rd(i);
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        if (i % 2)
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i % kReadAhead], df[i / 2], dp, 0, 0, 0);
+        else
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i % kReadAhead], qf[i / 2], s, 0, 0, 0);
+        if (i + kReadAhead < N) a[i % kReadAhead] = rd(i + kReadAhead);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     if (masked) {
       const int lim_t = lim - kt * TK - 4 * lg;
@@ -244,15 +260,21 @@ void bwd_dq_kernel(const BwdParams p) {
       const float p1 = __builtin_amdgcn_exp2f(fmaf(s[2 * j + 1], c2, nl2));
       dsk[j] = pack_bf16(p0 * (dp[2 * j] - ddv), p1 * (dp[2 * j + 1] - ddv));
     }
+    {  // dQ^T += K^T dS^T, transposed K operands read ahead in a fixed order
+      constexpr int N = 2 * NDB;
+      bf16x8 b[2];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const u32x4 bw = {dsk[4 * c], dsk[4 * c + 1], dsk[4 * c + 2], dsk[4 * c + 3]};
-      const bf16x8 b = __builtin_bit_cast(bf16x8, bw);
-      const __bf16* krows = kl + (16 * c) * D;
+      for (int c = 0; c < 2; ++c) b[c] = __builtin_bit_cast(bf16x8, u32x4{dsk[4 * c], dsk[4 * c + 1], dsk[4 * c + 2], dsk[4 * c + 3]});
+      auto rd = [&](int i) { return tr_operand(kl + 16 * (i / NDB) * D, tr_rd[0][i % NDB], tr_rd[1][i % NDB]); };
+      bf16x8 a[kReadAhead];
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(krows, tr_rd[0][db], tr_rd[1][db]), b, acc[db],
-                                                          0, 0, 0);
+      for (int i = 0; i < kReadAhead; ++i) a[i] = rd(i);
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        acc[i % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i % kReadAhead], b[i / NDB], acc[i % NDB], 0, 0, 0);
+        if (i + kReadAhead < N) a[i % kReadAhead] = rd(i + kReadAhead);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   };
 
@@ -415,11 +437,29 @@ void bwd_dkdv_kernel(const BwdParams p) {
     const __bf16* ql = lds + buf * 2 * TE;
     const __bf16* dl = ql + TE;
     f32x16 s = {}, dp = {};
+    {  // S^T and dP^T chains interleaved in a fixed order, operands (Q for even
+       // products; dO and the wave's V rows for odd ones) read kReadAhead ahead
+      constexpr int N = 2 * NC;
+      auto rd = [&](int i) { return *(const bf16x8*)((i % 2 ? dl : ql) + row_rd[i / 2]); };
+      auto rdv = [&](int i) { return *(const bf16x8*)(vlds + wave * 32 * D + row_rd[i / 2]); };
+      bf16x8 a[kReadAhead], bv[kReadAhead];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(ql + row_rd[c]), kf[c], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(dl + row_rd[c]),
-                                                   *(const bf16x8*)(vlds + wave * 32 * D + row_rd[c]), dp, 0, 0, 0);
+      for (int i = 0; i < kReadAhead; ++i) {
+        a[i] = rd(i);
+        if (i % 2) bv[i] = rdv(i);
+      }
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        if (i % 2)
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i % kReadAhead], bv[i % kReadAhead], dp, 0, 0, 0);
+        else
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i % kReadAhead], kf[i / 2], s, 0, 0, 0);
+        if (i + kReadAhead < N) {
+          a[i % kReadAhead] = rd(i + kReadAhead);
+          if ((i + kReadAhead) % 2) bv[i % kReadAhead] = rdv(i + kReadAhead);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     if (masked) {
       const int rbase_t = qt * TQ + 4 * lg;
@@ -444,18 +484,32 @@ void bwd_dkdv_kernel(const BwdParams p) {
       dsk[2 * j] = pack_bf16(pe[0] * (dp[4 * j] - dd[0]), pe[1] * (dp[4 * j + 1] - dd[1]));
       dsk[2 * j + 1] = pack_bf16(pe[2] * (dp[4 * j + 2] - dd[2]), pe[3] * (dp[4 * j + 3] - dd[3]));
     }
+    {  // dV^T += dO^T P^T and dK^T += Q^T dS^T interleaved, transposed
+       // operands read ahead in a fixed order
+      constexpr int N = 4 * NDB;
+      bf16x8 pw[2], sw[2];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const u32x4 pw = {pk[4 * c], pk[4 * c + 1], pk[4 * c + 2], pk[4 * c + 3]};
-      const u32x4 sw = {dsk[4 * c], dsk[4 * c + 1], dsk[4 * c + 2], dsk[4 * c + 3]};
-      const __bf16* drows = dl + (16 * c) * D;
-      const __bf16* qrows = ql + (16 * c) * D;
+      for (int c = 0; c < 2; ++c) {
+        pw[c] = __builtin_bit_cast(bf16x8, u32x4{pk[4 * c], pk[4 * c + 1], pk[4 * c + 2], pk[4 * c + 3]});
+        sw[c] = __builtin_bit_cast(bf16x8, u32x4{dsk[4 * c], dsk[4 * c + 1], dsk[4 * c + 2], dsk[4 * c + 3]});
+      }
+      // product i: rows 16 c (c = i / (2 NDB)), d block (i / 2) % NDB, dV (even) or dK (odd)
+      auto rd = [&](int i) {
+        const int c = i / (2 * NDB), db = (i / 2) % NDB;
+        return tr_operand((i % 2 ? ql : dl) + 16 * c * D, tr_rd[0][db], tr_rd[1][db]);
+      };
+      bf16x8 a[kReadAhead];
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(drows, tr_rd[0][db], tr_rd[1][db]),
-                                                         __builtin_bit_cast(bf16x8, pw), dv[db], 0, 0, 0);
-        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(qrows, tr_rd[0][db], tr_rd[1][db]),
-                                                         __builtin_bit_cast(bf16x8, sw), dk[db], 0, 0, 0);
+      for (int i = 0; i < kReadAhead; ++i) a[i] = rd(i);
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const int c = i / (2 * NDB), db = (i / 2) % NDB;
+        if (i % 2)
+          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i % kReadAhead], sw[c], dk[db], 0, 0, 0);
+        else
+          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i % kReadAhead], pw[c], dv[db], 0, 0, 0);
+        if (i + kReadAhead < N) a[i % kReadAhead] = rd(i + kReadAhead);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
