@@ -26,9 +26,11 @@
 //    ds_read_b64_tr_b16 of four consecutive keys each from row-major V.
 //  * K and V tiles stream through a ring of NB LDS buffers, filled straight
 //    from global memory (buffer_load ... lds) NB - 1 tiles ahead; the 16-byte
-//    units of each row are XOR swizzled with swz16 below so the K reads (16
-//    rows of one unit per 16 lanes) and the transposed V reads (8 rows of two
-//    adjacent units per 32 lanes) are free of bank conflicts.
+//    units of each row are XOR swizzled with swz16 below so the transposed V
+//    reads (8 rows of two adjacent units per 32 lanes) are free of bank
+//    conflicts.  The K reads (16 rows of one unit per 16 lanes, the four lane
+//    groups on four adjacent units of the same rows) measure 4 conflict cycles
+//    per read with this and every other bijective row swizzle tried.
 //  * Within a tile the matrix products run in a fixed order, each LDS operand
 //    read a few products ahead of its use; a wave's two phases (scores, then
 //    softmax and value products) overlap the other wave of its SIMD.
@@ -49,10 +51,10 @@ constexpr float kLazy = 8.0f;
 // Matrix products by which an LDS operand read runs ahead of its use.
 constexpr int kReadAhead = 4;
 
-// XOR swizzle of the low four bits of a 16-byte unit index in row r.  A
-// bijection on 16 consecutive rows (K reads), and for 8 consecutive rows
-// aligned to 8 it keeps bit 0 constant while bits 1..3 run through all values,
-// so two adjacent units of those rows land on 16 distinct bank groups (V reads).
+// XOR swizzle of the low four bits of a 16-byte unit index in row r: a
+// bijection on 16 consecutive rows, and for 8 consecutive rows aligned to 8 it
+// keeps bit 0 constant while bits 1..3 run through all values, so two adjacent
+// units of those rows land on 16 distinct bank groups (the V^T reads).
 __device__ __forceinline__ int swz16(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
 
 // Buffer resource words over `base` (no effective range limit; every access is
