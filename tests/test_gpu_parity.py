@@ -110,6 +110,30 @@ def test_fold_block_state_per_step(ra, dtype, d, q_rows, kv_rows):
         check_output(to64(o) / to64(l)[..., None], r.o / r.l[..., None], dtype, f"step {t} o/l")
 
 
+# Visiting-block lengths that take every path of the d = 256 kernel's tile loop
+# (32-key tiles through a three-deep LDS ring): a lone ragged tile, one full
+# tile, a full tile plus a ragged one, the groups of three full tiles, the
+# one-by-one remainder, and a ragged last tile after either.
+@pytest.mark.parametrize("kv_rows", [31, 32, 33, 64, 95, 96, 97, 128, 161, 224, 225])
+def test_fold_block_d256_tile_ring(ra, kv_rows):
+    _say(f"fold_block d=256 q_rows=130 kv_rows={kv_rows} seed=11")
+    B, H, q_rows, d, steps = 1, 2, 130, 256, 2
+    gen = torch.Generator(device="cuda").manual_seed(11 + kv_rows)
+    q = torch.randn((B, H, q_rows, d), generator=gen, device="cuda").to(torch.bfloat16)
+    ks = [torch.randn((B, H, kv_rows, d), generator=gen, device="cuda").mul(1.0 + t).to(torch.bfloat16) for t in range(steps)]
+    vs = [torch.randn((B, H, kv_rows, d), generator=gen, device="cuda").to(torch.bfloat16) for t in range(steps)]
+    m, l, o = _new_state(B, H, q_rows, d)
+    ra.ra_state_init(m, l, o)
+    ref = _oracle_steps(q, ks, vs)
+    for t in range(steps):
+        ra.ra_fold_block(q, ks[t], vs[t], m, l, o)
+        torch.cuda.synchronize()
+        r = ref[t]
+        np.testing.assert_allclose(to64(m), r.m, rtol=0, atol=2e-4 * (1 + np.abs(r.m).max()))
+        np.testing.assert_allclose(to64(l), r.l, rtol=1e-2)
+        check_output(to64(o) / to64(l)[..., None], r.o / r.l[..., None], "bf16", f"step {t} o/l")
+
+
 @pytest.mark.parametrize("d", [64, 128, 256])
 def test_fold_block_large_max_jumps(ra, d):
     """Scores whose running maximum jumps far (hundreds of base-2 units) inside
