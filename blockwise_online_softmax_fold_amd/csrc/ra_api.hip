@@ -188,12 +188,15 @@ Blocks ring_blocks(int64_t N, int32_t P) {
 // Workspace of the ring driver: state of the n_q resident blocks
 // (m, l: [B, H, rows]; o: [B, H, rows, d], rows = the residents' rows, at most
 // n_q * b_max) followed by the K and V halves of the double buffer, each
-// [slot][n_q][B][H][b_max][d].
+// [slot][B][H][n_q * b_max][d]: in each head, resident r's visiting block
+// starts at row r * b_max.  With every block resident in ring order and equal
+// blocks, a slot's head is then the whole sequence rotated by whole blocks,
+// which the hand-off fills with two contiguous copies.
 struct RingLayout {
   Blocks blk;
   int nslots = 0;
   size_t off_m = 0, off_l = 0, off_o = 0, off_k = 0, off_v = 0, total = 0;
-  int64_t res_elems = 0;   // K (or V) elements of one resident block's slot
+  int64_t head_rows = 0;   // rows of one (batch, head) in a slot: n_q * b_max
   int64_t slot_elems = 0;  // elements of one slot over all residents
 };
 
@@ -207,8 +210,8 @@ RingLayout ring_layout(ra_dtype_t dt, int64_t B, int64_t H, int64_t N, int64_t d
   L.off_l = round_up(L.off_m + st_rows * 4);
   L.off_o = round_up(L.off_l + st_rows * 4);
   L.off_k = round_up(L.off_o + st_rows * (size_t)d * 4);
-  L.res_elems = B * H * L.blk.b_max * d;
-  L.slot_elems = L.res_elems * n_q;
+  L.head_rows = (int64_t)n_q * L.blk.b_max;
+  L.slot_elems = B * H * L.head_rows * d;
   const size_t buf = (size_t)L.nslots * L.slot_elems * esize(dt);
   L.off_v = round_up(L.off_k + buf);
   L.total = round_up(L.off_v + buf);
@@ -248,14 +251,15 @@ void set_strides(int64_t* dst_b, int64_t* dst_h, int64_t* dst_r, const int64_t* 
 }
 
 // Copy rows [start, start + n) of src ([B, H, N, d] with strides s) into dst,
-// laid out [B][H][b_max][d] (the hand-off of one visiting block).
+// whose heads are dst_head_rows rows of d elements apart and whose batches are
+// H heads apart (the hand-off of one or more consecutive visiting blocks).
 ra_status_t copy_block(void* dst, const void* src, const int64_t* s, int64_t B, int64_t H, int64_t start, int64_t n,
-                       int64_t b_max, int64_t d, size_t es, hipStream_t stream) {
+                       int64_t dst_head_rows, int64_t d, size_t es, hipStream_t stream) {
   const char* sp = (const char*)src;
   char* dp = (char*)dst;
   const size_t row_bytes = (size_t)d * es;
   const size_t blk_bytes = (size_t)n * row_bytes;
-  const size_t dst_head = (size_t)b_max * row_bytes;
+  const size_t dst_head = (size_t)dst_head_rows * row_bytes;
   if (s[2] == d && (H == 1 || s[1] * (int64_t)es >= (int64_t)blk_bytes)) {
     // rows of a block are contiguous: one 2-D copy over heads per batch
     const size_t spitch = H == 1 ? blk_bytes : (size_t)s[1] * es;
@@ -528,6 +532,10 @@ ra_status_t ring_forward_impl(const void* q, const int64_t q_strides[3], const v
   }
   // Data for step t >= 1 lives in slot (t - 1) % 2.
   auto slot_of = [](int t) { return (t - 1) & 1; };
+  // Every block resident in ring order, all of one length: each slot head is
+  // the sequence rotated by whole blocks (two copies per batch and tensor).
+  bool rotated = n_q == P && bk.rem == 0;
+  for (int32_t r = 0; rotated && r < n_q; ++r) rotated = qb(r) == r;
 
   for (int t = 0; t < P; ++t) {
     if (t + 1 < P) {
@@ -535,13 +543,30 @@ ra_status_t ring_forward_impl(const void* q, const int64_t q_strides[3], const v
       // step t), issued before step t's fold so the two overlap.
       const int s = slot_of(t + 1);
       if (!serial && t + 1 >= 3) RA_HIP(hipStreamWaitEvent(side, dr->freed[s], 0), "hipStreamWaitEvent");
-      for (int32_t r = 0; r < n_q; ++r) {
-        const int64_t j = ((int64_t)qb(r) - (t + 1)) % P;
-        const int64_t jj = j < 0 ? j + P : j;
-        char* kd = kbuf + ((size_t)s * L.slot_elems + (size_t)r * L.res_elems) * es;
-        char* vd = vbuf + ((size_t)s * L.slot_elems + (size_t)r * L.res_elems) * es;
-        if ((st = copy_block(kd, k, k_strides, B, H, bk.start(jj), bk.len(jj), bm, d, es, side)) != RA_OK) return st;
-        if ((st = copy_block(vd, v, v_strides, B, H, bk.start(jj), bk.len(jj), bm, d, es, side)) != RA_OK) return st;
+      char* ks = kbuf + (size_t)s * L.slot_elems * es;
+      char* vs = vbuf + (size_t)s * L.slot_elems * es;
+      if (rotated) {
+        // Resident r visits block r - (t + 1): per head, slot rows [0, u b) are
+        // sequence rows [N - u b, N) and slot rows [u b, N) are rows [0, N - u b),
+        // u = t + 1.
+        const int64_t u = (int64_t)(t + 1) * bk.b;
+        const size_t off = (size_t)u * d * es;
+        if ((st = copy_block(ks, k, k_strides, B, H, N - u, u, L.head_rows, d, es, side)) != RA_OK) return st;
+        if ((st = copy_block(ks + off, k, k_strides, B, H, 0, N - u, L.head_rows, d, es, side)) != RA_OK) return st;
+        if ((st = copy_block(vs, v, v_strides, B, H, N - u, u, L.head_rows, d, es, side)) != RA_OK) return st;
+        if ((st = copy_block(vs + off, v, v_strides, B, H, 0, N - u, L.head_rows, d, es, side)) != RA_OK) return st;
+      } else {
+        for (int32_t r = 0; r < n_q; ++r) {
+          const int64_t j = ((int64_t)qb(r) - (t + 1)) % P;
+          const int64_t jj = j < 0 ? j + P : j;
+          const size_t off = (size_t)r * bm * d * es;
+          if ((st = copy_block(ks + off, k, k_strides, B, H, bk.start(jj), bk.len(jj), L.head_rows, d, es, side)) !=
+              RA_OK)
+            return st;
+          if ((st = copy_block(vs + off, v, v_strides, B, H, bk.start(jj), bk.len(jj), L.head_rows, d, es, side)) !=
+              RA_OK)
+            return st;
+        }
       }
       if (!serial) RA_HIP(hipEventRecord(dr->ready[s], side), "hipEventRecord");
     }
@@ -571,10 +596,10 @@ ra_status_t ring_forward_impl(const void* q, const int64_t q_strides[3], const v
         const int s = slot_of(t);
         p.k = kbuf + (size_t)s * L.slot_elems * es;
         p.v = vbuf + (size_t)s * L.slot_elems * es;
-        p.k_sb = p.v_sb = H * bm * d;
-        p.k_sh = p.v_sh = bm * d;
+        p.k_sb = p.v_sb = H * L.head_rows * d;
+        p.k_sh = p.v_sh = L.head_rows * d;
         p.k_sr = p.v_sr = d;
-        for (int32_t r = 0; r < nr; ++r) p.k_off[r] = p.v_off[r] = (int64_t)(r0 + r) * L.res_elems;
+        for (int32_t r = 0; r < nr; ++r) p.k_off[r] = p.v_off[r] = (int64_t)(r0 + r) * bm * d;
       }
       p.B = (int32_t)B;
       p.H = (int32_t)H;
