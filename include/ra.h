@@ -180,7 +180,10 @@ size_t ra_ring_workspace_bytes(ra_dtype_t dt, int64_t B, int64_t H, int64_t N, i
  * block in place; the next block is copied into the other half of a per-block
  * double buffer by hipMemcpy2DAsync on a side stream while the current step's
  * fold runs (the stand-in for the ring's send to i+1 / receive from i-1),
- * ordered by events.
+ * ordered by events.  When every block is resident in ring order
+ * (query_blocks NULL or 0..P-1) and P divides N, the blocks of one step are the
+ * sequence rotated by whole blocks, and the hand-off copies it as two
+ * contiguous pieces per batch and tensor instead of block by block.
  * workspace: device buffer of at least ra_ring_workspace_bytes(...) bytes,
  *      256-byte aligned, or NULL to let the library allocate and free one in
  *      stream order.  Two calls that share a workspace must be ordered on
