@@ -164,10 +164,29 @@ def _blas_threads() -> int:
     return len(os.sched_getaffinity(0))
 
 
-def cpu_baseline(w, q, k, v, seconds: float) -> dict:
+def parity_figures(got, ref, dtype: str) -> dict:
+    """Error of the timed run's output rows against the oracle's, with the
+    bar the parity tests apply (bf16: max-abs <= 2e-2 and mean-abs <= 2e-3;
+    fp32: max-abs <= 1e-5 max|ref|)."""
+    import numpy as np
+
+    err = np.abs(np.asarray(got, dtype=np.float64) - ref)
+    max_abs, mean_abs = float(err.max()), float(err.mean())
+    if dtype == "bf16":
+        ok = max_abs <= 2e-2 and mean_abs <= 2e-3
+        bar = "max-abs <= 2e-2, mean-abs <= 2e-3"
+    else:
+        ok = max_abs <= 1e-5 * float(np.abs(ref).max())
+        bar = "max-abs <= 1e-5 max|ref|"
+    return {"max_abs": max_abs, "mean_abs": mean_abs, "within_bar": bool(ok), "bar": bar}
+
+
+def cpu_baseline(w, q, k, v, seconds: float, out=None) -> dict:
     """Time the fp64 oracle (as it stands) on a bounded sample of the same
     workload: whole query rows against all N keys of one head, in chunks, until
-    about ``seconds`` of CPU work.  Rate in the metric's unit (TFLOP/s)."""
+    about ``seconds`` of CPU work.  Rate in the metric's unit (TFLOP/s).  With
+    ``out`` (the timed run's output) the rows the oracle computed are also
+    compared with it: the bench line carries its own parity figure."""
     import numpy as np
     import torch
 
@@ -178,14 +197,25 @@ def cpu_baseline(w, q, k, v, seconds: float) -> dict:
     q64 = q[0, 0].to("cpu", torch.float64).numpy()
     chunk = 256
     rows_done, elapsed, r0 = 0, 0.0, 0
+    ref_rows, ref_vals = [], []
     while elapsed < seconds and rows_done < q64.shape[0]:
         qs = q64[r0:r0 + chunk]
         t0 = time.perf_counter()
-        oracle.dense_attention(qs, k64, v64)
+        o_ref = oracle.dense_attention(qs, k64, v64)
         elapsed += time.perf_counter() - t0
+        if out is not None:
+            ref_rows.append(np.arange(r0, r0 + qs.shape[0]))
+            ref_vals.append(o_ref)
         rows_done += qs.shape[0]
         r0 = (r0 + chunk) % q64.shape[0]
     flops = 4.0 * rows_done * w.N * w.d
+    parity = None
+    if out is not None:
+        rows = np.concatenate(ref_rows)
+        got = out[0, 0, torch.from_numpy(rows).to(out.device)].to("cpu", torch.float64).numpy()
+        parity = parity_figures(got, np.concatenate(ref_vals), w.dtype)
+        parity["rows"] = int(len(rows))
+        parity["sample"] = f"head 0, query rows {int(rows.min())}..{int(rows.max())} of the timed run's output"
     # the naive ring loop (init, P folds in ring order, finalize) on rows of
     # query block 0, for about a third of the time
     from oracle import ring as oring
@@ -216,6 +246,7 @@ def cpu_baseline(w, q, k, v, seconds: float) -> dict:
                       "sample": f"fp64 naive ring loop, {ring_rows} rows of query block 0 folding all "
                                 f"{w.P} blocks ({ring_elapsed:.1f} s)"},
         "host_cpus": len(os.sched_getaffinity(0)),
+        "parity": parity,
     }
 
 
@@ -276,6 +307,24 @@ class ClockSampler:
 XGMI_LINK_GBPS = 153.0  # one MI355X xGMI link, one direction (GB/s)
 
 
+def min_block_for_overlap(flop_rate: float, link_bytes_per_s: float, elem_bytes: int = 2) -> float:
+    """Smallest block c (tokens per device) whose fold hides the next K/V block's
+    transfer (vibeengines.com "Ring attention, explained", method step 7 and
+    "At the extremes"): a step folds c keys into c queries, 4 d c^2 FLOP, while
+    the next block, K and V of c rows of d elements, 2 c d elem_bytes bytes,
+    crosses the link; the transfer hides when 4 d c^2 / F >= 2 c d e / B, i.e.
+    c >= F e / (2 B), which is F / B for 16-bit elements (d cancels)."""
+    return flop_rate * elem_bytes / (2.0 * link_bytes_per_s)
+
+
+def links_needed(fold_flops: float, fold_s: float, kv_bytes: float, link_bytes_per_s: float) -> float:
+    """How many links' bandwidth one ring step needs to hide its hand-off behind
+    a fold of fold_flops FLOP that takes fold_s seconds: transfer time over one
+    link divided by the fold time (<= 1: one link hides it).  Equals
+    min_block_for_overlap(fold_flops / fold_s, link) / c for a c-token block."""
+    return (kv_bytes / link_bytes_per_s) / fold_s
+
+
 def device_sweep(torch, ra, steps: int, warmup: int) -> int:
     """One device's share of a ring step: fold one visiting block of b keys into
     the state of the resident block's b query rows (B1 H32 d128 bf16), timed with
@@ -318,7 +367,8 @@ def device_sweep(torch, ra, steps: int, warmup: int) -> int:
         row = {"b": b, "fold_ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
                "fold_no_spill_ms": round(ms_nospill, 4), "spill_share": round(1.0 - ms_nospill / ms, 4),
                "kv_block_mb": round(kv_bytes / 1e6, 2), "xgmi_1link_ms": round(xfer_ms, 4),
-               "links_needed": round(xfer_ms / ms, 2)}
+               "links_needed": round(links_needed(flops, ms * 1e-3, kv_bytes, XGMI_LINK_GBPS * 1e9), 2),
+               "min_b_one_link": round(min_block_for_overlap(flops / (ms * 1e-3), XGMI_LINK_GBPS * 1e9))}
         print(f"[bench] device sweep {row}", file=sys.stderr, flush=True)
         rows.append(row)
         del q, k, v, m, l, o, out, ws
@@ -494,9 +544,14 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         print(f"[bench] timing the CPU oracle for ~{args.cpu_seconds:.0f} s", file=sys.stderr, flush=True)
-        rec["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
+        # the output rows the oracle computes are checked against the last timed
+        # step's output (full attention, forward only: what the oracle computes)
+        check = out if not (args.backward or args.causal) else None
+        rec["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds, out=check)
+        rec["parity"] = rec["cpu_baseline"].pop("parity")
     else:
         rec["cpu_baseline"] = None
+        rec["parity"] = None
     print(json.dumps(rec), flush=True)
     return 0
 

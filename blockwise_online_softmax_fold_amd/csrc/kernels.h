@@ -161,6 +161,8 @@ hipError_t launch_bwd_prep(const float* lse, const void* dout, int64_t do_sb, in
 // dst = alpha * acc ([B, H, rows, d] fp32, contiguous) in the output dtype with strides.
 hipError_t launch_scale_cast(const float* acc, float alpha, void* dst, int64_t sb, int64_t sh, int64_t sr, bool bf16,
                              int B, int H, int64_t rows, int d, hipStream_t s);
+// Fill `bytes` bytes (a multiple of 16, 16-byte aligned) with a repeated 32-bit word.
+hipError_t launch_fill_u32(void* x, size_t bytes, unsigned value, hipStream_t s);
 // Fill n floats with zero.
 hipError_t launch_zero(float* x, int64_t n, hipStream_t s);
 // out element (bi, hi, row, c) = o / l, 0 where l == 0; out_bf16 selects the output type.

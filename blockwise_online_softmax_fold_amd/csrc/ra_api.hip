@@ -8,6 +8,7 @@
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
+#include <time.h>
 
 #include <map>
 #include <mutex>
@@ -322,6 +323,25 @@ bool env_flag(const char* name) {
   return v != nullptr && v[0] != '\0' && v[0] != '0';
 }
 
+long env_long(const char* name) {
+  const char* v = getenv(name);
+  return v == nullptr ? 0 : strtol(v, nullptr, 10);
+}
+
+// Host callback of the delayed hand-off (RA_DEBUG_DELAY_US): holds the side
+// stream for the given number of microseconds.
+void sleep_cb(void* us) {
+  const long n = (long)(intptr_t)us;
+  struct timespec ts;
+  ts.tv_sec = n / 1000000;
+  ts.tv_nsec = (n % 1000000) * 1000;
+  nanosleep(&ts, nullptr);
+}
+
+// Quiet NaN patterns of a poisoned hand-off slot, as 32-bit words.
+constexpr unsigned kNanBf16x2 = 0x7fc07fc0u;
+constexpr unsigned kNanF32 = 0x7fc00000u;
+
 }  // namespace
 
 RA_API const char* ra_last_error(void) { return g_err.c_str(); }
@@ -523,6 +543,14 @@ ra_status_t ring_forward_impl(const void* q, const int64_t q_strides[3], const v
   const int64_t bm = bk.b_max;
 
   const bool serial = env_flag("RA_SYNC_EACH_STEP");
+  // Hand-off hazard checks (debug modes for eager calls; not for graph capture):
+  // RA_DEBUG_POISON fills each slot with NaN on the caller's stream right after
+  // the fold that reads it, so a refill ordered too early (a missing "freed"
+  // edge) or a fold that does not wait for its copy (a missing "ready" edge)
+  // shows up as NaN in the output; RA_DEBUG_DELAY_US holds the side stream
+  // that long before each hand-off, so a missing "ready" edge reads stale data.
+  const bool poison = env_flag("RA_DEBUG_POISON");
+  const long delay_us = env_long("RA_DEBUG_DELAY_US");
   hipStream_t side = serial ? stream : dr->side;
   if (!serial) {
     RA_HIP(hipEventRecord(dr->fork, stream), "hipEventRecord");
@@ -545,6 +573,8 @@ ra_status_t ring_forward_impl(const void* q, const int64_t q_strides[3], const v
       if (!serial && t + 1 >= 3) RA_HIP(hipStreamWaitEvent(side, dr->freed[s], 0), "hipStreamWaitEvent");
       char* ks = kbuf + (size_t)s * L.slot_elems * es;
       char* vs = vbuf + (size_t)s * L.slot_elems * es;
+      if (delay_us > 0)
+        RA_HIP(hipLaunchHostFunc(side, sleep_cb, (void*)(intptr_t)delay_us), "hipLaunchHostFunc (delayed hand-off)");
       if (rotated) {
         // Resident r visits block r - (t + 1): per head, slot rows [0, u b) are
         // sequence rows [N - u b, N) and slot rows [u b, N) are rows [0, N - u b),
@@ -625,6 +655,12 @@ ra_status_t ring_forward_impl(const void* q, const int64_t q_strides[3], const v
       const long pi = prof_begin(stream);
       RA_HIP(launch_fold(p, dt, (int)d, stream), "fold launch");
       prof_end(pi, stream);
+    }
+    if (poison && t >= 1) {
+      const size_t slot_bytes = (size_t)L.slot_elems * es;
+      const unsigned nan = dt == RA_DTYPE_BF16 ? kNanBf16x2 : kNanF32;
+      RA_HIP(ra::launch_fill_u32(kbuf + (size_t)slot_of(t) * slot_bytes, slot_bytes, nan, stream), "poison launch");
+      RA_HIP(ra::launch_fill_u32(vbuf + (size_t)slot_of(t) * slot_bytes, slot_bytes, nan, stream), "poison launch");
     }
     // The slot read by this step is refilled two steps later.
     if (t >= 1 && t + 2 <= P - 1 && !serial) RA_HIP(hipEventRecord(dr->freed[slot_of(t)], stream), "hipEventRecord");
@@ -740,6 +776,19 @@ RA_API ra_status_t ra_ring_backward(const void* q, const int64_t q_strides[3], c
   if ((st = check_tensor("dv", dv, dv_strides, dt)) != RA_OK) return st;
   if (lse == nullptr) return fail(RA_E_INVALID_ARG, "lse is NULL");
   if (((uintptr_t)lse & 3) != 0) return fail(RA_E_INVALID_ARG, "lse is not 4-byte aligned");
+  // Two residents of one block would visit the same key block in the same
+  // step, and the dK/dV kernel gives each tile of keys to one workgroup per
+  // resident with no atomics: their read-modify-writes of dk_acc / dv_acc
+  // would race.  A ring holds each block once, so duplicates are refused.
+  if (query_blocks != nullptr) {
+    std::vector<char> seen(P, 0);
+    for (int32_t r = 0; r < n_q; ++r) {
+      if (seen[query_blocks[r]])
+        return fail(RA_E_INVALID_ARG, "query_blocks[%d]=%d repeats a block; the backward needs distinct blocks",
+                    (int)r, (int)query_blocks[r]);
+      seen[query_blocks[r]] = 1;
+    }
+  }
   float sc;
   if ((st = resolve_scale(scale, d, &sc)) != RA_OK) return st;
   const BwdLayout L = bwd_layout(B, H, N, d, P, n_q);

@@ -121,6 +121,13 @@ __global__ __launch_bounds__(256) void zero_kernel(float* x, int64_t n_vec4) {
     ((f32x4*)x)[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 }
 
+__global__ __launch_bounds__(256) void fill_kernel(unsigned* x, int64_t n_vec4, unsigned value) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_vec4; i += stride)
+    ((u32x4*)x)[i] = u32x4{value, value, value, value};
+}
+
 inline unsigned grid_for(int64_t n) {
   const int64_t g = (n + 255) / 256;
   return (unsigned)(g < 1 ? 1 : (g > 65536 ? 65536 : g));
@@ -170,6 +177,14 @@ hipError_t launch_scale_cast(const float* acc, float alpha, void* dst, int64_t s
     scale_cast_kernel<true><<<grid_for(n_vec4), 256, 0, s>>>(acc, alpha, dst, sb, sh, sr, H, rows, d, n_vec4);
   else
     scale_cast_kernel<false><<<grid_for(n_vec4), 256, 0, s>>>(acc, alpha, dst, sb, sh, sr, H, rows, d, n_vec4);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_u32(void* x, size_t bytes, unsigned value, hipStream_t s) {
+  if (bytes % 16 != 0 || ((uintptr_t)x & 15) != 0) return hipErrorInvalidValue;
+  const int64_t n_vec4 = (int64_t)(bytes / 16);
+  if (n_vec4 <= 0) return hipSuccess;
+  fill_kernel<<<grid_for(n_vec4), 256, 0, s>>>((unsigned*)x, n_vec4, value);
   return hipGetLastError();
 }
 

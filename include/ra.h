@@ -242,7 +242,10 @@ size_t ra_ring_backward_workspace_bytes(ra_dtype_t dt, int64_t B, int64_t H, int
  * With P = softmax weights rebuilt from lse: dV = P^T dO, dP = dO V^T,
  * D = rowsum(dO * O), dS = P * (dP - D), dQ = scale dS K, dK = scale dS^T Q.
  *
- * q, k, v, layout, query_blocks, n_q, scale: exactly as given to the forward.
+ * q, k, v, layout, query_blocks, n_q, scale: exactly as given to the forward;
+ *      the block ids in query_blocks must be distinct (RA_E_INVALID_ARG
+ *      otherwise: two residents of one block would add to the same dK, dV rows
+ *      at once).
  * out, lse: the forward's output and log-sum-exp (ra_ring_forward_ex).
  * dout: dL/dO, like out.  dq: like q, receives dL/dQ of the resident rows.
  * dk, dv: [B, H, N, d] like k and v, overwritten with the resident blocks'

@@ -223,6 +223,19 @@ def test_ring_backward_rejects(lib, kwargs, status, needle):
     assert needle in lib.ra_last_error().decode()
 
 
+def test_ring_backward_rejects_repeated_blocks(lib):
+    """Two residents of one block would race on that block's dK/dV
+    accumulators; the backward refuses them (the forward allows them)."""
+    S = S_BF16
+    P = 4
+    for qb in ((1, 1), (0, 2, 3, 2)):
+        arr = (ctypes.c_int32 * len(qb))(*qb)
+        st = lib.ra_ring_backward(A, S, A, S, A, S, A, S, A, S, A, A, S, A, S, A, S, BF16, 1, 16, 4096, 128, P, arr,
+                                  len(qb), ctypes.c_float(0.0), 0, ctypes.c_void_p(None), 0, None)
+        assert st == 1
+        assert "repeats a block" in lib.ra_last_error().decode()
+
+
 def test_ring_backward_workspace_size(lib):
     B, H, N, d, P = 1, 2, 1000, 64, 3
     got = lib.ra_ring_backward_workspace_bytes(BF16, B, H, N, d, P, P)

@@ -105,3 +105,39 @@ def test_more_than_one_gpu_is_refused():
     assert res.returncode == 2
     assert "one GPU" in res.stderr
     assert res.stdout == ""
+
+
+def test_overlap_condition_matches_the_pages_a100_figures():
+    """vibeengines.com "At the extremes": at 312 TFLOP/s over a ~300 GB/s link a
+    block of about 1,000 tokens (312e12 / 300e9 = 1040) hides the transfer; at
+    12.5 GB/s it takes about 25,000 (24,960)."""
+    assert bench.min_block_for_overlap(312e12, 300e9) == pytest.approx(1040.0)
+    assert bench.min_block_for_overlap(312e12, 12.5e9) == pytest.approx(24960.0)
+    # 32-bit elements move twice the bytes: twice the block
+    assert bench.min_block_for_overlap(312e12, 300e9, elem_bytes=4) == pytest.approx(2080.0)
+
+
+@pytest.mark.parametrize("c,d", [(1040, 128), (1040, 64), (8192, 128), (520, 256)])
+def test_links_needed_is_one_exactly_at_the_threshold(c, d):
+    """At F = 312 TFLOP/s and B = 300 GB/s a c-token step needs c_min / c links:
+    one link exactly at c = 1040 whatever d is, half at twice the block."""
+    F, Bw = 312e12, 300e9
+    flops = 4.0 * d * c * c
+    kv_bytes = 2.0 * c * d * 2
+    n = bench.links_needed(flops, flops / F, kv_bytes, Bw)
+    assert n == pytest.approx(bench.min_block_for_overlap(F, Bw) / c)
+    if c == 1040:
+        assert n == pytest.approx(1.0)
+
+
+def test_parity_figures_apply_the_bars():
+    import numpy as np
+
+    ref = np.linspace(-1, 1, 64).reshape(4, 16)
+    ok = bench.parity_figures(ref + 1e-3, ref, "bf16")
+    assert ok["within_bar"] and ok["max_abs"] == pytest.approx(1e-3)
+    bad = ref.copy()
+    bad[0, 0] += 0.05
+    assert not bench.parity_figures(bad, ref, "bf16")["within_bar"]
+    assert bench.parity_figures(ref * (1 + 5e-6), ref, "f32")["within_bar"]
+    assert not bench.parity_figures(ref * (1 + 5e-5), ref, "f32")["within_bar"]
