@@ -8,6 +8,8 @@ include/ra.h); this package is its thin ctypes binding:
 * ``ra_finalize``    -- O = o / l
 * ``ra_ring_forward`` -- all P virtual ring steps for the resident query blocks,
   with the double-buffered K/V hand-off on a side stream
+* ``ra_ring_forward_noalloc`` -- the same in the library's static device
+  scratch (``NOALLOC_SCRATCH_BYTES``), for callers that cannot allocate
 * ``ra_fold_block_causal``, ``ra_ring_forward_causal`` -- the same under a
   causal mask, for contiguous, striped or zig-zag token layouts
 * ``ra_ring_forward_ex`` -- the forward that also returns each row's log-sum-exp
@@ -19,6 +21,7 @@ include/ra.h); this package is its thin ctypes binding:
 from .binding import (
     CAUSAL_LAYOUTS,
     EXPORTED,
+    NOALLOC_SCRATCH_BYTES,
     RA_DTYPE_BF16,
     RA_DTYPE_F32,
     RaError,
@@ -35,6 +38,7 @@ from .binding import (
     ra_ring_backward_workspace_bytes,
     ra_ring_forward_causal,
     ra_ring_forward_ex,
+    ra_ring_forward_noalloc,
     ra_ring_workspace_bytes,
     ra_state_init,
     ra_version,
@@ -43,6 +47,7 @@ from .binding import (
 __all__ = [
     "CAUSAL_LAYOUTS",
     "EXPORTED",
+    "NOALLOC_SCRATCH_BYTES",
     "RA_DTYPE_BF16",
     "RA_DTYPE_F32",
     "RaError",
@@ -59,6 +64,7 @@ __all__ = [
     "ra_ring_backward_workspace_bytes",
     "ra_ring_forward_causal",
     "ra_ring_forward_ex",
+    "ra_ring_forward_noalloc",
     "ra_ring_workspace_bytes",
     "ra_state_init",
     "ra_version",

@@ -39,6 +39,7 @@ EXPORTED = (
     "ra_finalize",
     "ra_ring_workspace_bytes",
     "ra_ring_forward",
+    "ra_ring_forward_noalloc",
     "ra_ring_forward_causal",
     "ra_ring_forward_ex",
     "ra_ring_backward_workspace_bytes",
@@ -92,6 +93,9 @@ def load() -> ctypes.CDLL:
     lib.ra_ring_forward.argtypes = [vp, strides, vp, strides, vp, strides, vp, strides, ctypes.c_int, i64, i64, i64,
                                     i64, i32, ctypes.POINTER(ctypes.c_int32), i32, f32, vp, sz, vp]
     lib.ra_ring_forward.restype = ctypes.c_int
+    lib.ra_ring_forward_noalloc.argtypes = [vp, strides, vp, strides, vp, strides, vp, strides, ctypes.c_int, i64,
+                                            i64, i64, i64, i32, ctypes.POINTER(ctypes.c_int32), i32, f32, vp]
+    lib.ra_ring_forward_noalloc.restype = ctypes.c_int
     lib.ra_ring_forward_causal.argtypes = [vp, strides, vp, strides, vp, strides, vp, strides, ctypes.c_int, i64,
                                            i64, i64, i64, i32, ctypes.POINTER(ctypes.c_int32), i32, f32,
                                            ctypes.c_int, vp, sz, vp]
@@ -265,6 +269,18 @@ def ra_ring_forward(q, k, v, P: int, query_blocks: Sequence[int] | None = None, 
     return _ring(q, k, v, P, query_blocks, out, scale, workspace, stream, None)
 
 
+#: bytes of the static scratch ra_ring_forward_noalloc runs in (RA_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def ra_ring_forward_noalloc(q, k, v, P: int, query_blocks: Sequence[int] | None = None, out=None,
+                            scale: float = 0.0, stream=None):
+    """ra_ring_forward in the library's static device scratch: allocates
+    nothing (``out`` must then be given by a caller that cannot allocate).
+    Rings needing more than NOALLOC_SCRATCH_BYTES of workspace are refused."""
+    return _ring(q, k, v, P, query_blocks, out, scale, None, stream, None, noalloc=True)
+
+
 def ra_ring_forward_causal(q, k, v, P: int, layout, query_blocks: Sequence[int] | None = None, out=None,
                            scale: float = 0.0, workspace=None, stream=None):
     """The causal ring: q, k, v in ``layout``'s device order; returns out."""
@@ -340,7 +356,7 @@ def _ring_shape_check(q, k, v, P, query_blocks):
                              f"got {tuple(q.shape)}")
 
 
-def _ring(q, k, v, P, query_blocks, out, scale, workspace, stream, layout, lse=None):
+def _ring(q, k, v, P, query_blocks, out, scale, workspace, stream, layout, lse=None, noalloc=False):
     import torch
 
     B, H, N, d = k.shape
@@ -360,7 +376,9 @@ def _ring(q, k, v, P, query_blocks, out, scale, workspace, stream, layout, lse=N
         raise TypeError("q, k, v and out must have one dtype")
     args = (_dev(q, "q"), _strides(q), _dev(k, "k"), _strides(k), _dev(v, "v"), _strides(v), _dev(out, "out"),
             _strides(out), _dtype_code(q), B, H, N, d, int(P), qb, n_q, float(scale))
-    if lse is not None:
+    if noalloc:
+        _check(load().ra_ring_forward_noalloc(*args, _stream(stream)))
+    elif lse is not None:
         _check(load().ra_ring_forward_ex(*args[:8], _dev(lse, "lse"), *args[8:], _layout_code(layout), ws_ptr,
                                          ws_bytes, _stream(stream)))
     elif layout is None:

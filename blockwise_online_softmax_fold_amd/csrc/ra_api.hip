@@ -105,6 +105,14 @@ ra_status_t resolve_scale(float scale, int64_t d, float* out) {
 
 float to_log2_scale(float scale) { return (float)((double)scale * 1.4426950408889634); }
 
+// Device scratch of ra_ring_forward_noalloc: the ring workspace for callers
+// that cannot allocate.  Each GPU holds its own copy from the time the library
+// is first used on it until the process ends.  In host code the name below is
+// not a device address; the address comes from hipGetSymbolAddress, once per
+// device (DevRes::scratch).
+constexpr size_t kScratchBytes = RA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 // Per-device resources owned by the library: the side stream of the hand-off
 // and the events ordering it against the caller's stream.
 struct DevRes {
@@ -112,6 +120,7 @@ struct DevRes {
   hipEvent_t fork = nullptr, join = nullptr;
   hipEvent_t ready[2] = {nullptr, nullptr};
   hipEvent_t freed[2] = {nullptr, nullptr};
+  void* scratch = nullptr;  // this device's address of `scratch`, once resolved
   std::mutex mu;  // one ring driver at a time per device uses these
 };
 
@@ -493,11 +502,13 @@ RA_API size_t ra_ring_workspace_bytes(ra_dtype_t dt, int64_t B, int64_t H, int64
 
 namespace {
 
+// use_scratch: run in the device's static scratch (ra_ring_forward_noalloc)
+// instead of `workspace`, which must then be NULL.
 ra_status_t ring_forward_impl(const void* q, const int64_t q_strides[3], const void* k, const int64_t k_strides[3],
                               const void* v, const int64_t v_strides[3], void* out, const int64_t out_strides[3],
                               ra_dtype_t dt, int64_t B, int64_t H, int64_t N, int64_t d, int32_t P,
                               const int32_t* query_blocks, int32_t n_q, float scale, int mask, float* lse,
-                              void* workspace, size_t workspace_bytes, void* stream_) {
+                              void* workspace, size_t workspace_bytes, void* stream_, bool use_scratch = false) {
   ra_status_t st = check_ring(q, q_strides, k, k_strides, v, v_strides, out, out_strides, dt, B, H, N, d, P,
                               query_blocks, n_q);
   if (st != RA_OK) return st;
@@ -506,6 +517,11 @@ ra_status_t ring_forward_impl(const void* q, const int64_t q_strides[3], const v
   float sc;
   if ((st = resolve_scale(scale, d, &sc)) != RA_OK) return st;
   const RingLayout L = ring_layout(dt, B, H, N, d, P, n_q);
+  if (use_scratch && L.total > kScratchBytes)
+    return fail(RA_E_INVALID_ARG,
+                "this ring needs %zu bytes of workspace, more than the %zu-byte static scratch of "
+                "ra_ring_forward_noalloc",
+                L.total, kScratchBytes);
   if (workspace != nullptr) {
     if (workspace_bytes < L.total)
       return fail(RA_E_INVALID_ARG, "workspace of %zu bytes is smaller than the %zu bytes needed", workspace_bytes,
@@ -528,6 +544,16 @@ ra_status_t ring_forward_impl(const void* q, const int64_t q_strides[3], const v
   cleanup.stream = stream;
 
   void* ws = workspace;
+  if (use_scratch) {
+    // Resolved once per device, with that device current (get_dev found the
+    // current device's resources); the array's name is never used as an address.
+    if (dr->scratch == nullptr) {
+      void* ptr = nullptr;
+      RA_HIP(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "hipGetSymbolAddress (scratch)");
+      dr->scratch = ptr;
+    }
+    ws = dr->scratch;
+  }
   const bool own_ws = ws == nullptr;
   if (own_ws) {
     RA_HIP(hipMallocAsync(&ws, L.total, stream), "hipMallocAsync (ring workspace)");
@@ -687,6 +713,16 @@ RA_API ra_status_t ra_ring_forward(const void* q, const int64_t q_strides[3], co
   g_err.clear();
   return ring_forward_impl(q, q_strides, k, k_strides, v, v_strides, out, out_strides, dt, B, H, N, d, P,
                            query_blocks, n_q, scale, ra::kMaskNone, nullptr, workspace, workspace_bytes, stream);
+}
+
+RA_API ra_status_t ra_ring_forward_noalloc(const void* q, const int64_t q_strides[3], const void* k,
+                                           const int64_t k_strides[3], const void* v, const int64_t v_strides[3],
+                                           void* out, const int64_t out_strides[3], ra_dtype_t dt, int64_t B,
+                                           int64_t H, int64_t N, int64_t d, int32_t P, const int32_t* query_blocks,
+                                           int32_t n_q, float scale, void* stream) {
+  g_err.clear();
+  return ring_forward_impl(q, q_strides, k, k_strides, v, v_strides, out, out_strides, dt, B, H, N, d, P,
+                           query_blocks, n_q, scale, ra::kMaskNone, nullptr, nullptr, 0, stream, true);
 }
 
 RA_API ra_status_t ra_ring_forward_causal(const void* q, const int64_t q_strides[3], const void* k,

@@ -196,6 +196,32 @@ ra_status_t ra_ring_forward(const void* q, const int64_t q_strides[3], const voi
                             size_t workspace_bytes, void* stream);
 
 /*
+ * ra_ring_forward_noalloc -- ra_ring_forward for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, checks, schedule and kernels as
+ * ra_ring_forward with a NULL workspace, but the workspace is a static device
+ * array of RA_NOALLOC_SCRATCH_BYTES bytes inside the library instead of an
+ * allocation: the call allocates and frees nothing.
+ *   * A ring whose ra_ring_workspace_bytes(...) exceeds RA_NOALLOC_SCRATCH_BYTES
+ *     is rejected with RA_E_INVALID_ARG before any GPU work.
+ *   * Each GPU the library runs on holds its own copy of the array until the
+ *     process ends; its address is resolved on the first call on that device,
+ *     which also creates the device's side stream and events (as the first
+ *     ring call of any kind does): make that first call outside graph capture.
+ *   * Every call on one GPU shares that GPU's array and leaves the last call's
+ *     contents in it; nothing in it needs to start at zero (each call writes
+ *     every byte it reads).  Calls that may run at the same time on one GPU
+ *     (on different streams, or captured in graphs launched concurrently) race
+ *     on it: order them.
+ */
+#define RA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+ra_status_t ra_ring_forward_noalloc(const void* q, const int64_t q_strides[3], const void* k,
+                                    const int64_t k_strides[3], const void* v, const int64_t v_strides[3], void* out,
+                                    const int64_t out_strides[3], ra_dtype_t dt, int64_t B, int64_t H, int64_t N,
+                                    int64_t d, int32_t P, const int32_t* query_blocks, int32_t n_q, float scale,
+                                    void* stream);
+
+/*
  * ra_ring_forward_causal -- ra_ring_forward under a causal mask.  q, k, v and
  * out are in the layout's device order: block j is device j's share, holding
  * the positions given above for `layout` (contiguous: block j's first

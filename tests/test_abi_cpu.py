@@ -249,3 +249,23 @@ def test_ring_forward_ex_rejects_misaligned_lse(lib):
     st = lib.ra_ring_forward_ex(A, S_BF16, A, S_BF16, A, S_BF16, A, S_BF16, ctypes.c_void_p(0x10001), BF16, 1, 32,
                                 131072, 128, 16, None, 16, ctypes.c_float(0.0), 0, ctypes.c_void_p(None), 0, None)
     assert st == 1 and "lse" in lib.ra_last_error().decode()
+
+
+def test_noalloc_refuses_rings_beyond_its_scratch_on_the_host(lib):
+    """ra_ring_forward_noalloc runs in a static scratch of RA_NOALLOC_SCRATCH_BYTES
+    (64 MiB); a ring needing more workspace is refused before any HIP call."""
+    import blockwise_online_softmax_fold_amd as ra
+
+    assert ra.NOALLOC_SCRATCH_BYTES == 64 << 20
+    text = open(HEADER).read()
+    assert "#define RA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)" in text
+    need = lib.ra_ring_workspace_bytes(BF16, 1, 16, 16384, 128, 8, 8)
+    assert need > ra.NOALLOC_SCRATCH_BYTES
+    st = lib.ra_ring_forward_noalloc(A, S_BF16, A, S_BF16, A, S_BF16, A, S_BF16, BF16, 1, 16, 16384, 128, 8, None, 8,
+                                     ctypes.c_float(0.0), None)
+    assert st == 1
+    assert "static scratch" in lib.ra_last_error().decode()
+    # and argument checks come first, as in ra_ring_forward
+    st = lib.ra_ring_forward_noalloc(A, S_BF16, A, S_BF16, A, S_BF16, A, S_BF16, BF16, 1, 16, 16384, 96, 8, None, 8,
+                                     ctypes.c_float(0.0), None)
+    assert st == 2 and "head dim" in lib.ra_last_error().decode()
