@@ -374,7 +374,10 @@ void fold_bf16_kernel(const FoldParams p) {
     const float l_tot = pair_sum(lpart[g]) * fix;
     if (!row_ok[g]) continue;
     if (p.flags & kWriteOut) {
-      const float inv = l_tot > 0.0f ? fix / l_tot : 0.0f;
+      // (o fix) (1 / l): the state the step would store, then ra_finalize's
+      // normalisation, so a ring equals the same folds followed by ra_finalize
+      // bit for bit
+      const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
       if (p.lse != nullptr && lg == 0)
         p.lse[st_row[g]] = l_tot > 0.0f ? (mtrue[g] + __log2f(l_tot)) * kLn2 : -INFINITY;
       __bf16* orow = (__bf16*)p.out + bi * p.out_sb + hi * p.out_sh + srow[g] * p.out_sr + 4 * lg;
@@ -384,7 +387,7 @@ void fold_bf16_kernel(const FoldParams p) {
         for (int j = 0; j < 4; ++j) {
           bf16x4 t;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) t[e] = (__bf16)(oacc[g][db][4 * j + e] * inv);
+          for (int e = 0; e < 4; ++e) t[e] = (__bf16)((oacc[g][db][4 * j + e] * fix) * inv);
           *(bf16x4*)(orow + 32 * db + 8 * j) = t;
         }
     }

@@ -26,11 +26,9 @@
 //    ds_read_b64_tr_b16 of four consecutive keys each from row-major V.
 //  * K and V tiles stream through a ring of NB LDS buffers, filled straight
 //    from global memory (buffer_load ... lds) NB - 1 tiles ahead; the 16-byte
-//    units of each row are XOR swizzled with swz16 below so the transposed V
-//    reads (8 rows of two adjacent units per 32 lanes) are free of bank
-//    conflicts.  The K reads (16 rows of one unit per 16 lanes, the four lane
-//    groups on four adjacent units of the same rows) measure 4 conflict cycles
-//    per read with this and every other bijective row swizzle tried.
+//    units of each row are XOR swizzled so that neither the transposed V reads
+//    (8 rows of two adjacent units per 32 lanes, swz16 below) nor the K reads
+//    (16 rows of one unit per 16 lanes, swz16_k below) meet a bank conflict.
 //  * Within a tile the matrix products run in a fixed order, each LDS operand
 //    read a few products ahead of its use; a wave's two phases (scores, then
 //    softmax and value products) overlap the other wave of its SIMD.
@@ -57,6 +55,16 @@ constexpr int kReadAhead = 4;
 // units of those rows land on 16 distinct bank groups (the V^T reads).
 __device__ __forceinline__ int swz16(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
 
+// Row swizzle of the K tile.  gfx950 serves a ds_read_b128 in four groups of
+// 16 lanes, lanes l and l' sharing a group when bit 5 and the parity of bits
+// 2..4 of l and l' agree (measured: a read costs one pass per group exactly
+// when no two lanes of a group touch the same 16-byte bank group).  A K read
+// puts row lr = l % 16 and unit 4 e + l / 16 on lane l, so a group holds
+// every row once, with bit 0 of its unit index flipped by bits 2 ^ 3 of the
+// row; XORing that parity into swz16 makes the group's 16 bank groups distinct
+// (with swz16 alone they pair up: two passes per group).
+__device__ __forceinline__ int swz16_k(int r) { return swz16(r) ^ (((r >> 2) ^ (r >> 3)) & 1); }
+
 // Buffer resource words over `base` (no effective range limit; every access is
 // computed in bounds by the kernel), held in scalar registers.
 __device__ __forceinline__ u32x4 rsrc_words(const void* base) {
@@ -72,12 +80,13 @@ __device__ __forceinline__ u32x4 rsrc_words(const void* base) {
 // tell which LDS bytes such a load writes, does not make every later LDS read
 // wait for it; the tile loop waits for the loads itself (s_waitcnt vmcnt, then
 // a barrier) before any wave reads them.  The instruction has no destination
-// registers.  Every LDS load of the kernel goes through here, so the compiler
-// never sets M0 itself.
+// registers.  M0 is an operand of the statement ("{m0}"), so the compiler
+// writes it and knows it is taken; the s_nop is the wait state the hardware
+// needs between an SALU write of M0 and an LDS-direct load that reads it.
 __device__ __forceinline__ void dma16(u32x4 rsrc, int voff, unsigned lds_addr) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
-               : "s"(lds_addr), "v"(voff), "s"(rsrc)
+               : "v"(voff), "s"(rsrc), "{m0}"(lds_addr)
                : "memory");
 }
 
@@ -142,6 +151,55 @@ void fold_bf16_r16_kernel(const FoldParams p) {
   const int64_t srow = (int64_t)p.q_row0[r] + (row_ok ? row : q_len - 1);
   const int64_t st_row = ((int64_t)bi * p.H + hi) * p.st_bh + srow;
 
+  const __bf16* kbase = (const __bf16*)p.k + bi * p.k_sb + hi * p.k_sh + p.k_off[r];
+  const __bf16* vbase = (const __bf16*)p.v + bi * p.v_sb + hi * p.v_sh + p.v_off[r];
+  const int n_plain = min(kv_all, kv_len) / TK;
+  const int n_kt = (kv_vis + TK - 1) / TK;
+  const float c2 = p.scale_log2;
+
+  // Direct loads: chunk j of this wave is LDS units [64 (wave CPW + j), +64);
+  // lane i writes unit u = (row, pos) and fetches global unit pos ^ swz16_k(row)
+  // of K, pos ^ swz16(row) of V.
+  const int k_sr = (int)p.k_sr, v_sr = (int)p.v_sr;
+  int ld_koff[CPW], ld_voff[CPW];
+#pragma unroll
+  for (int j = 0; j < CPW; ++j) {
+    const int u = (wave * CPW + j) * 64 + lane;
+    const int lrow = u / UPR;
+    ld_koff[j] = (lrow * k_sr + ((u % UPR) ^ swz16_k(lrow)) * 8) * 2;
+    ld_voff[j] = (lrow * v_sr + ((u % UPR) ^ swz16(lrow)) * 8) * 2;
+  }
+  // LDS byte address of this wave's first chunk in buffer 0 (wave-uniform).
+  const unsigned lds_wave = (unsigned)__builtin_amdgcn_readfirstlane(
+      (unsigned)(size_t)(__attribute__((address_space(3))) __bf16*)lds + wave * CPW * 1024);
+  auto issue_tile = [&](int kt, int buf) {
+    const int key0 = kt * TK;
+    const unsigned kl = lds_wave + buf * 4 * TE;  // bytes
+    const unsigned vl = kl + 2 * TE;
+    const u32x4 kr = rsrc_words(kbase + (int64_t)key0 * k_sr);
+    const u32x4 vr = rsrc_words(vbase + (int64_t)key0 * v_sr);
+    if (key0 + TK <= kv_len) {
+#pragma unroll
+      for (int j = 0; j < CPW; ++j) {
+        dma16(kr, ld_koff[j], kl + j * 1024);
+        dma16(vr, ld_voff[j], vl + j * 1024);
+      }
+    } else {  // ragged last tile: rows past the end re-read the last row
+#pragma unroll
+      for (int j = 0; j < CPW; ++j) {
+        const int u = (wave * CPW + j) * 64 + lane;
+        const int lrow = u / UPR;
+        const int rr = min(lrow, kv_len - 1 - key0);
+        dma16(kr, (rr * k_sr + ((u % UPR) ^ swz16_k(lrow)) * 8) * 2, kl + j * 1024);
+        dma16(vr, (rr * v_sr + ((u % UPR) ^ swz16(lrow)) * 8) * 2, vl + j * 1024);
+      }
+    }
+  };
+
+  // Tile 0 is requested before Q and the state, so the three loads' latencies
+  // overlap.
+  if (n_kt > 0) issue_tile(0, 0);
+
   bf16x8 qf[NC];
   {
     const __bf16* qp = (const __bf16*)p.q + bi * p.q_sb + hi * p.q_sh + srow * p.q_sr + 8 * lg;
@@ -170,55 +228,9 @@ void fold_bf16_r16_kernel(const FoldParams p) {
   }
   mtrue = mref;
 
-  const __bf16* kbase = (const __bf16*)p.k + bi * p.k_sb + hi * p.k_sh + p.k_off[r];
-  const __bf16* vbase = (const __bf16*)p.v + bi * p.v_sb + hi * p.v_sh + p.v_off[r];
-  const int n_plain = min(kv_all, kv_len) / TK;
-  const int n_kt = (kv_vis + TK - 1) / TK;
-  const float c2 = p.scale_log2;
-
-  // Direct loads: chunk j of this wave is LDS units [64 (wave CPW + j), +64);
-  // lane i writes unit u = (row, pos) and fetches global unit pos ^ swz16(row).
-  const int k_sr = (int)p.k_sr, v_sr = (int)p.v_sr;
-  int ld_koff[CPW], ld_voff[CPW];
-#pragma unroll
-  for (int j = 0; j < CPW; ++j) {
-    const int u = (wave * CPW + j) * 64 + lane;
-    const int lrow = u / UPR;
-    const int gunit = (u % UPR) ^ swz16(lrow);
-    ld_koff[j] = (lrow * k_sr + gunit * 8) * 2;
-    ld_voff[j] = (lrow * v_sr + gunit * 8) * 2;
-  }
-  // LDS byte address of this wave's first chunk in buffer 0 (wave-uniform).
-  const unsigned lds_wave = (unsigned)__builtin_amdgcn_readfirstlane(
-      (unsigned)(size_t)(__attribute__((address_space(3))) __bf16*)lds + wave * CPW * 1024);
-  auto issue_tile = [&](int kt, int buf) {
-    const int key0 = kt * TK;
-    const unsigned kl = lds_wave + buf * 4 * TE;  // bytes
-    const unsigned vl = kl + 2 * TE;
-    const u32x4 kr = rsrc_words(kbase + (int64_t)key0 * k_sr);
-    const u32x4 vr = rsrc_words(vbase + (int64_t)key0 * v_sr);
-    if (key0 + TK <= kv_len) {
-#pragma unroll
-      for (int j = 0; j < CPW; ++j) {
-        dma16(kr, ld_koff[j], kl + j * 1024);
-        dma16(vr, ld_voff[j], vl + j * 1024);
-      }
-    } else {  // ragged last tile: rows past the end re-read the last row
-#pragma unroll
-      for (int j = 0; j < CPW; ++j) {
-        const int u = (wave * CPW + j) * 64 + lane;
-        const int lrow = u / UPR;
-        const int gunit = (u % UPR) ^ swz16(lrow);
-        const int rr = min(lrow, kv_len - 1 - key0);
-        dma16(kr, (rr * k_sr + gunit * 8) * 2, kl + j * 1024);
-        dma16(vr, (rr * v_sr + gunit * 8) * 2, vl + j * 1024);
-      }
-    }
-  };
-
   // K operand of chunk c = 4 h + e (global unit 16 h + 4 e + lg of row lr):
-  // LDS element lr D + 128 h + (((4 e + lg) ^ swz16(lr)) << 3).
-  const int ks = swz16(lr);
+  // LDS element lr D + 128 h + (((4 e + lg) ^ swz16_k(lr)) << 3).
+  const int ks = swz16_k(lr);
   int k_rd[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) k_rd[e] = lr * D + (((4 * e + lg) ^ ks) << 3);
@@ -346,13 +358,14 @@ void fold_bf16_r16_kernel(const FoldParams p) {
     values(pa, vc);
   };
 
-  // Q and the state have landed before any tile load is in flight, so the
-  // compiler's own waits for them stay outside the tile loop (where they would
-  // also wait for the tile loads the compiler does not see).
+  // Q, the state and tile 0 land before the tile loop, so the compiler's own
+  // waits for Q and the state stay outside it (inside, they would also wait
+  // for the tile loads the compiler does not see).  Tile 0 was issued before
+  // them, so those waits are never too short.
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   if (n_kt > 0) {
 #pragma unroll
-    for (int t = 0; t < NB - 1; ++t)
+    for (int t = 1; t < NB - 1; ++t)
       if (t < n_kt) issue_tile(t, t);
     // Full-depth, unmasked tiles in groups of NB (compile-time buffers), then
     // the rest one by one.
@@ -369,14 +382,15 @@ void fold_bf16_r16_kernel(const FoldParams p) {
   const float l_tot = quad_sum(lpart) * fix;
   if (!row_ok) return;
   if (p.flags & kWriteOut) {
-    const float inv = l_tot > 0.0f ? fix / l_tot : 0.0f;
+    // (o fix) (1 / l): the stored state, then ra_finalize's normalisation
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     if (p.lse != nullptr && lg == 0) p.lse[st_row] = l_tot > 0.0f ? (mtrue + __log2f(l_tot)) * kLn2 : -INFINITY;
     __bf16* orow = (__bf16*)p.out + bi * p.out_sb + hi * p.out_sh + srow * p.out_sr + 4 * lg;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       bf16x4 t;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) t[e] = (__bf16)(oacc[db][e] * inv);
+      for (int e = 0; e < 4; ++e) t[e] = (__bf16)((oacc[db][e] * fix) * inv);
       *(bf16x4*)(orow + 16 * db) = t;
     }
   }
