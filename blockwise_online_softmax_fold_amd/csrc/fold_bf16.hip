@@ -60,6 +60,15 @@ using namespace dev;
 
 // Lazy rescaling threshold (base-2 units): weights stay below 2^kLazy.
 constexpr float kLazy = 8.0f;
+// With the reference state (kRefState), a tile's weights are first taken
+// against the current reference without looking at the tile's maximum.  A
+// lane's 32 weights summing to at most 2^kLazy bounds each of them by 2^kLazy,
+// as the maximum test would; a larger sum (some weight above 2^kLazy / 32 =
+// 2^(kLazy - 5)) sends the wave through the maximum, a raise of the reference
+// for the rows whose maximum exceeds it by more than kLazy - 5, and the
+// weights again.
+constexpr float kRefSum = 256.0f;  // 2^kLazy
+constexpr float kRefRaise = 3.0f;  // kLazy - 5
 
 // Keys per LDS tile.
 constexpr int kTileKeys = 64;
@@ -72,7 +81,9 @@ constexpr int kReadAhead = 2;
 // in a loop unrolled by two, so both LDS buffers have compile-time offsets; a
 // ragged last tile runs once after it, with key masking.  The per-wave state
 // is written for G groups of 32 query rows; one group per wave is used.
-template <int D, int NW>
+// REF: the state is kept relative to the reference maximum (kRefState): no
+// per-tile maximum unless the weights' sums call for one, no true maximum.
+template <int D, int NW, bool REF>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void fold_bf16_kernel(const FoldParams p) {
   constexpr int G = 1;  // query groups of 32 rows per wave
@@ -121,7 +132,7 @@ void fold_bf16_kernel(const FoldParams p) {
     kv_all = last_key(q_first) + 1;
     lim = min(lim, last_key(min(q_first + wave * 32 * G + lr, q_len - 1)));
     // Nothing visible and nothing to initialise or write: the state stays as it is.
-    if (kv_vis == 0 && p.flags == (kLoadState | kStoreState)) return;
+    if (kv_vis == 0 && (p.flags & ~kRefState) == (kLoadState | kStoreState)) return;
   }
 
   int64_t srow[G], st_row[G];
@@ -145,14 +156,15 @@ void fold_bf16_kernel(const FoldParams p) {
   // mref: the reference maximum the weights are taken against (base-2 units
   // of the scaled score); it trails the true running maximum mtrue by less
   // than kLazy, which keeps every weight below 2^kLazy.  o and l are rescaled
-  // to mtrue once, before they are stored.
+  // to mtrue once, before they are stored; with REF they stay relative to
+  // mref, which is stored as it is (base 2) and mtrue is not tracked.
   float mref[G], mtrue[G], lpart[G], m_in[G];
   f32x16 oacc[G][NDB];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     if (p.flags & kLoadState) {
       m_in[g] = p.m[st_row[g]];
-      mref[g] = m_in[g] * kLog2e;
+      mref[g] = REF ? m_in[g] : m_in[g] * kLog2e;
       lpart[g] = lg == 0 ? p.l[st_row[g]] : 0.0f;
       const float* orow = p.o + st_row[g] * D + 4 * lg;
 #pragma unroll
@@ -296,7 +308,7 @@ void fold_bf16_kernel(const FoldParams p) {
   // bf16 weights exp2(s c - mref) as packed pairs, and their sum into l.  A
   // row that has seen no visible key yet (mref = -inf, every score -inf) gets
   // weights exp2(-inf) = 0.
-  auto weights = [&](const f32x16 (&s)[NKB], unsigned (&pk)[NKB][8], int g) {
+  auto weights = [&](const f32x16 (&s)[NKB], unsigned (&pk)[NKB][8], int g) -> float {
     const float mr = mref[g] == -INFINITY ? 0.0f : mref[g];
     float lsum = 0.0f;
 #pragma unroll
@@ -308,7 +320,30 @@ void fold_bf16_kernel(const FoldParams p) {
         pk[kb][j] = pack_bf16(p0, p1);
         lsum = sum_bf16_pair(pk[kb][j], lsum);
       }
-    lpart[g] += lsum;
+    return lsum;
+  };
+  // REF: the slow path of a tile.  Row maximum of the tile; a row that has
+  // seen no key yet takes it as its reference, a row whose maximum exceeds
+  // the reference by more than kRefRaise raises it (o and l rescaled here).
+  auto settle_ref = [&](const f32x16 (&s)[NKB], int g) {
+    float mx = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+    const float mt = pair_max(mx) * c2;
+    const bool fresh = mref[g] == -INFINITY;
+    const bool raise = !fresh && mt > mref[g] + kRefRaise;
+    if (fresh) mref[g] = mt;
+    if (__builtin_amdgcn_ballot_w64(raise)) {
+      const float alpha = raise ? __builtin_amdgcn_exp2f(mref[g] - mt) : 1.0f;
+      if (raise) mref[g] = mt;
+      lpart[g] *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[g][db][i] *= alpha;
+    }
   };
   // O^T += V^T P^T over the tile, 16 keys per product, in the same fixed
   // order with each V^T operand (two transposed reads) read ahead.
@@ -348,8 +383,21 @@ void fold_bf16_kernel(const FoldParams p) {
     unsigned pa[NKB][8];
     scores(sa, kc, 0);
     if (masked) mask(sa, kt * TK);
-    track_max(sa, 0);
-    weights(sa, pa, 0);
+    if constexpr (REF) {
+      // The weights against the current reference; the wave settles the
+      // maximum first only if a lane's sum exceeds 2^kLazy (or is not a
+      // number) or a row that has seen no key yet sees one in this tile.
+      float ls = weights(sa, pa, 0);
+      const bool fresh_vis = mref[0] == -INFINITY && lim >= kt * TK;
+      if (__builtin_amdgcn_ballot_w64(fresh_vis || !(ls <= kRefSum))) {
+        settle_ref(sa, 0);
+        ls = weights(sa, pa, 0);
+      }
+      lpart[0] += ls;
+    } else {
+      track_max(sa, 0);
+      lpart[0] += weights(sa, pa, 0);
+    }
     values(pa, vc, 0);
   };
 
@@ -369,8 +417,10 @@ void fold_bf16_kernel(const FoldParams p) {
 
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    // Bring (l, o) from the reference maximum to the true running maximum.
-    const float fix = mref[g] == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(mref[g] - mtrue[g]);
+    // Bring (l, o) from the reference maximum to the true running maximum
+    // (REF: they stay relative to the reference).
+    const float fix = REF || mref[g] == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(mref[g] - mtrue[g]);
+    const float mrow = REF ? mref[g] : mtrue[g];  // the maximum (l, o) are relative to
     const float l_tot = pair_sum(lpart[g]) * fix;
     if (!row_ok[g]) continue;
     if (p.flags & kWriteOut) {
@@ -379,7 +429,7 @@ void fold_bf16_kernel(const FoldParams p) {
       // bit for bit
       const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
       if (p.lse != nullptr && lg == 0)
-        p.lse[st_row[g]] = l_tot > 0.0f ? (mtrue[g] + __log2f(l_tot)) * kLn2 : -INFINITY;
+        p.lse[st_row[g]] = l_tot > 0.0f ? (mrow + __log2f(l_tot)) * kLn2 : -INFINITY;
       __bf16* orow = (__bf16*)p.out + bi * p.out_sb + hi * p.out_sh + srow[g] * p.out_sr + 4 * lg;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
@@ -393,8 +443,9 @@ void fold_bf16_kernel(const FoldParams p) {
     }
     if (p.flags & kStoreState) {
       if (lg == 0) {
-        // A maximum that did not rise is stored exactly as it was loaded.
-        p.m[st_row[g]] = mtrue[g] == m_in[g] * kLog2e ? m_in[g] : mtrue[g] * kLn2;
+        // A maximum that did not rise is stored exactly as it was loaded; the
+        // reference (REF) is stored in base 2 as it is.
+        p.m[st_row[g]] = REF ? mref[g] : mtrue[g] == m_in[g] * kLog2e ? m_in[g] : mtrue[g] * kLn2;
         p.l[st_row[g]] = l_tot;
       }
       float* orow = p.o + st_row[g] * D + 4 * lg;
@@ -424,12 +475,19 @@ hipError_t launch_fold_bf16(const FoldParams& p, int d, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   const dim3 gd((unsigned)grid), bd(waves_for(d) * 64);
+  const bool ref = (p.flags & kRefState) != 0;
   switch (d) {
     case 64:
-      fold_bf16_kernel<64, waves_for(64)><<<gd, bd, 0, s>>>(p);
+      if (ref)
+        fold_bf16_kernel<64, waves_for(64), true><<<gd, bd, 0, s>>>(p);
+      else
+        fold_bf16_kernel<64, waves_for(64), false><<<gd, bd, 0, s>>>(p);
       break;
     case 128:
-      fold_bf16_kernel<128, waves_for(128)><<<gd, bd, 0, s>>>(p);
+      if (ref)
+        fold_bf16_kernel<128, waves_for(128), true><<<gd, bd, 0, s>>>(p);
+      else
+        fold_bf16_kernel<128, waves_for(128), false><<<gd, bd, 0, s>>>(p);
       break;
     default:
       return hipErrorInvalidValue;

@@ -143,7 +143,7 @@ void fold_bf16_r16_kernel(const FoldParams p) {
     kv_vis = last_key(q_last) + 1;
     kv_all = last_key(q_first) + 1;
     lim = min(lim, last_key(min(q_first + wave * 16 + lr, q_len - 1)));
-    if (kv_vis == 0 && p.flags == (kLoadState | kStoreState)) return;
+    if (kv_vis == 0 && (p.flags & ~kRefState) == (kLoadState | kStoreState)) return;
   }
 
   const int row = qt * QT + wave * 16 + lr;

@@ -66,7 +66,7 @@ __global__ __launch_bounds__(256) void fold_f32_kernel(const FoldParams p) {
     kv_vis = last_key(min(qt * ROWS + ROWS, q_len) - 1) + 1;
     lim = min(lim, last_key(min(row, q_len - 1)));
     // Nothing visible and nothing to initialise or write: the state stays as it is.
-    if (kv_vis == 0 && p.flags == (kLoadState | kStoreState)) return;
+    if (kv_vis == 0 && (p.flags & ~kRefState) == (kLoadState | kStoreState)) return;
   }
   const int64_t srow = (int64_t)p.q_row0[r] + (row_ok ? row : q_len - 1);
   const int col0 = CPL * sub;

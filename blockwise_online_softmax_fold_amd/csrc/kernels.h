@@ -15,6 +15,13 @@ enum FoldFlags : int {
   kLoadState = 1,   // read (m, l, o) from the state arrays; else start from (-inf, 0, 0)
   kStoreState = 2,  // write (m, l, o) back (the spill between ring steps)
   kWriteOut = 4,    // write O = o / l to `out` instead (the last step of the ring)
+  // The spilled state is internal to a ring: m may hold the reference maximum
+  // the weights were taken against (base 2, at most the running maximum) with
+  // l and o relative to it, instead of the running maximum itself.  O and the
+  // log-sum-exp are the same either way.  fold_bf16_kernel (d = 64, 128) keeps
+  // the reference; the other kernels ignore the flag and keep the running
+  // maximum, which is one such state too.
+  kRefState = 8,
 };
 
 // One fold launch: n_res resident query blocks; resident r has q_len[r] query

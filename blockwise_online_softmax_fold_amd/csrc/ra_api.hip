@@ -660,7 +660,9 @@ ra_status_t ring_forward_impl(const void* q, const int64_t q_strides[3], const v
       p.B = (int32_t)B;
       p.H = (int32_t)H;
       p.n_res = nr;
-      p.flags = (t == 0 ? 0 : ra::kLoadState) | (t == P - 1 ? ra::kWriteOut : ra::kStoreState);
+      // The spilled state never leaves the ring, so it may stay relative to
+      // the kernels' reference maximum (kRefState).
+      p.flags = (t == 0 ? 0 : ra::kLoadState) | (t == P - 1 ? ra::kWriteOut : ra::kStoreState) | ra::kRefState;
       p.scale_log2 = to_log2_scale(sc);
       p.mask = mask;
       p.P = P;

@@ -274,10 +274,37 @@ def test_checkpoint_resume_bitwise(ra):
     a, c = run(-1), run(2)
     torch.cuda.synchronize()
     assert torch.equal(a, c)
-    # the fold_block loop equals ring_forward for that block
+    # the fold_block loop agrees with ring_forward for that block; not bit for
+    # bit: inside the ring the spilled state stays relative to the kernel's
+    # reference maximum (kRefState), while fold_block's state is relative to
+    # the running maximum, so the bf16 weights round differently
     full = ra.ra_ring_forward(q_all, k, v, P)
     torch.cuda.synchronize()
-    assert torch.equal(full[:, :, i * b:(i + 1) * b], a)
+    check_output(full[:, :, i * b:(i + 1) * b], to64(a), "bf16", "ring vs fold_block loop")
+
+
+def test_ring_rising_max_every_step(ra):
+    """Resident block 0 of a P = 8 ring whose visiting blocks arrive with scores
+    6 higher at every step (natural units): every step raises the running
+    maximum by about 8.7 in base 2, so inside the ring each step's first tile
+    takes the reference-raising path (the weights' sums exceed 2^8).  The
+    output against the oracle; the math page's worked example is this rescale,
+    repeated."""
+    _say("ring_forward rising max every step, bf16 B1 H2 N8192 d128 P8, resident block 0")
+    P, B, H, N, d = 8, 1, 2, 8192, 128
+    b = N // P
+    gen = torch.Generator(device="cuda").manual_seed(91)
+    u = torch.randn((d,), generator=gen, device="cuda")
+    u = u / torch.linalg.vector_norm(u)
+    q = (torch.randn((B, H, b, d), generator=gen, device="cuda") + math.sqrt(d) * u).bfloat16()
+    # block j carries shift 6 ((P - j) mod P): resident 0 visits j = 0, P-1, ..., 1
+    shift = torch.tensor([6.0 * ((P - j) % P) for j in range(P)], device="cuda").repeat_interleave(b)
+    k = (torch.randn((B, H, N, d), generator=gen, device="cuda") + shift[:, None] * u).bfloat16()
+    v = (torch.rand((B, H, N, d), generator=gen, device="cuda") * 2 - 1).bfloat16()
+    out = ra.ra_ring_forward(q, k, v, P, query_blocks=[0])
+    torch.cuda.synchronize()
+    ref = oracle.dense_attention(to64(q), to64(k), to64(v))
+    check_output(out, ref, "bf16", "rising max, resident 0")
 
 
 def test_fold_order_invariance(ra):
