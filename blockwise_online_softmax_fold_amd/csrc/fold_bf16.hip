@@ -98,6 +98,14 @@ void fold_bf16_kernel(const FoldParams p) {
   static_assert(CPW >= 1 && TE % (512 * NW) == 0, "tile must split into whole 1 KB chunks per wave");
   __shared__ __attribute__((aligned(1024))) __bf16 lds[2 * 2 * TE];
 
+  // The launch-wide arguments every path reads, loaded here in one round of
+  // scalar loads: left to itself the compiler loads each at its first use,
+  // behind the branches below, one round trip after another.
+  asm volatile("" ::"s"(p.B), "s"(p.H), "s"(p.n_res), "s"(p.q_rows), "s"(p.flags), "s"(p.mask), "s"(p.scale_log2),
+               "s"(p.q), "s"(p.k), "s"(p.v), "s"(p.o), "s"(p.m), "s"(p.l), "s"(p.q_sb), "s"(p.q_sh), "s"(p.q_sr),
+               "s"(p.k_sb), "s"(p.k_sh), "s"(p.k_sr), "s"(p.v_sb), "s"(p.v_sh), "s"(p.v_sr), "s"(p.st_bh), "s"(p.P),
+               "s"(p.blk), "s"(p.rem));
+
   const int tiles_q = (p.q_rows + QT - 1) / QT;
   const int total = tiles_q * p.n_res * p.H * p.B;
   int w = xcd_remap(blockIdx.x, total);
@@ -114,8 +122,13 @@ void fold_bf16_kernel(const FoldParams p) {
   const int lr = lane & 31;
   const int lg = lane >> 5;
 
-  // This resident's block lengths; a query tile past its end has nothing to do.
+  // This resident's block lengths and offsets, all read here, before any
+  // branch, so their scalar loads go out together; a query tile past the
+  // block's end has nothing to do.
   const int q_len = p.q_len[r], kv_len = p.kv_len[r];
+  const int64_t q_row0 = p.q_row0[r], k_off = p.k_off[r], v_off = p.v_off[r];
+  const int q_blk = p.q_blk[r], kv_blk = p.kv_blk[r];
+  asm volatile("" ::"s"(q_len), "s"(kv_len), "s"(q_row0), "s"(k_off), "s"(v_off), "s"(q_blk), "s"(kv_blk));
   if (qt * QT >= q_len) return;
 
   // Keys [0, kv_vis) are visible to some row of this workgroup, keys
@@ -123,7 +136,7 @@ void fold_bf16_kernel(const FoldParams p) {
   int kv_vis = kv_len, kv_all = kv_len;
   int lim = kv_len - 1;
   if (p.mask != kMaskNone) {
-    const int qb = p.q_blk[r], kb = p.kv_blk[r];
+    const int qb = q_blk, kb = kv_blk;
     const int q_first = qt * QT, q_last = min(q_first + QT, q_len) - 1;
     auto last_key = [&](int qrow) {
       return last_key_at_or_before(p.mask, p.P, p.blk, p.rem, kb, token_pos(p.mask, p.P, p.blk, p.rem, qb, qrow));
@@ -141,7 +154,7 @@ void fold_bf16_kernel(const FoldParams p) {
   for (int g = 0; g < G; ++g) {
     const int row = qt * QT + wave * 32 * G + g * 32 + lr;
     row_ok[g] = row < q_len;
-    srow[g] = (int64_t)p.q_row0[r] + (row_ok[g] ? row : q_len - 1);
+    srow[g] = q_row0 + (row_ok[g] ? row : q_len - 1);
     st_row[g] = ((int64_t)bi * p.H + hi) * p.st_bh + srow[g];
   }
 
@@ -187,8 +200,8 @@ void fold_bf16_kernel(const FoldParams p) {
     mtrue[g] = mref[g];
   }
 
-  const __bf16* kbase = (const __bf16*)p.k + bi * p.k_sb + hi * p.k_sh + p.k_off[r];
-  const __bf16* vbase = (const __bf16*)p.v + bi * p.v_sb + hi * p.v_sh + p.v_off[r];
+  const __bf16* kbase = (const __bf16*)p.k + bi * p.k_sb + hi * p.k_sh + k_off;
+  const __bf16* vbase = (const __bf16*)p.v + bi * p.v_sb + hi * p.v_sh + v_off;
   // Tiles [0, n_plain) need no mask; tiles [n_plain, n_kt) compare keys with lim.
   const int n_plain = min(kv_all, kv_len) / TK;
   const int n_kt = (kv_vis + TK - 1) / TK;
