@@ -184,6 +184,11 @@ size_t ra_ring_workspace_bytes(ra_dtype_t dt, int64_t B, int64_t H, int64_t N, i
  * (query_blocks NULL or 0..P-1) and P divides N, the blocks of one step are the
  * sequence rotated by whole blocks, and the hand-off copies it as two
  * contiguous pieces per batch and tensor instead of block by block.
+ * The (m, l, o) spilled between the ring's steps stays inside the workspace;
+ * for bf16 with d = 64 or 128 it is kept relative to a reference maximum at
+ * most the running maximum (raised lazily) instead of the running maximum
+ * itself.  O equals that of the same folds through ra_fold_block followed by
+ * ra_finalize up to rounding, not bit for bit.
  * workspace: device buffer of at least ra_ring_workspace_bytes(...) bytes,
  *      256-byte aligned, or NULL to let the library allocate and free one in
  *      stream order.  Two calls that share a workspace must be ordered on
