@@ -43,7 +43,7 @@ if ROOT not in sys.path:
 
 METRIC = "ring-fold attention TFLOP/s and % MFMA bf16 peak, 128K tokens P=16, 1 GPU"
 PEAK = {"bf16": 2500.0, "f32": 157.3}  # MI355X published dense TFLOP/s: bf16 MFMA, fp32 vector
-FOLD_SOURCES = {"bf16": "fold_bf16.hip", "f32": "fold_f32.hip", "bf16/d256": "fold_bf16_r16.hip"}
+FOLD_SOURCES = {"bf16": "fold_bf16.hip", "f32": "fold_f32.hip"}
 BWD_SOURCES = {"bf16": "fold_bwd_bf16.hip", "f32": "fold_bwd_f32.hip"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fold_traffic.json")
 
@@ -513,7 +513,6 @@ def main() -> int:
         "frac": round(achieved / peak, 4),
         "traffic": None if args.causal else _traffic(w.name, w.dtype, args.backward, w.d),
         "kernel": (f"bwd_dq_kernel<{w.d}> + bwd_dkdv_kernel<{w.d}> (one step)" if args.backward
-                   else f"fold_bf16_r16_kernel<{w.d}>" if (w.dtype, w.d) == ("bf16", 256)
                    else f"fold_{w.dtype}_kernel<{w.d}>"),
         "flop_per_launch": flops_per_launch,
         "avg_launch_ms": round(fold_avg_ms, 4),

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libra.so")
 C_CLIENT_SRC = os.path.join(ROOT, "tests", "c", "ring_forward_c.c")
 C_CLIENT_PATH = os.path.join(PKG_DIR, "ring_forward_c")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
-SOURCES = ["ra_api.hip", "fold_bf16.hip", "fold_bf16_r16.hip", "fold_f32.hip", "fold_bwd_bf16.hip", "fold_bwd_f32.hip", "state.hip"]
+SOURCES = ["ra_api.hip", "fold_bf16.hip", "fold_f32.hip", "fold_bwd_bf16.hip", "fold_bwd_f32.hip", "state.hip"]
 ARCH = "gfx950"
 
 

@@ -7,20 +7,22 @@
 // l' = alpha l + sum exp(s - m'), o' = alpha o + sum exp(s - m') v.
 //
 // Mapping onto CDNA4:
-//  * d = 64 and 128 (d = 256 runs the 16-row kernel of fold_bf16_r16.hip,
-//    whose state fits two waves per SIMD).
-//  * A workgroup is NW waves (8 for d = 128, 4 for d = 64); each wave
+//  * A workgroup is NW waves (8 for d = 128, 4 for d = 64 and 256); each wave
 //    owns 32 query rows, so a workgroup owns a 32 NW-row query tile, and every
 //    K/V tile brought into LDS (and through L2) serves all of them.  With 8
-//    waves one workgroup fills a CU at two waves per SIMD.  Q stays in
+//    waves one workgroup fills a CU at two waves per SIMD; at d = 256 the 32
+//    rows' Q and o take 192 registers, so two 4-wave workgroups share a CU
+//    (measured faster on a 1024-key visiting block than one 8-wave workgroup:
+//    while one loads or stores its state the other computes).  Q stays in
 //    registers as MFMA operands for the whole launch; the state (m, l, o) is
 //    loaded once, kept in registers while the visiting block streams past, and
 //    stored once (or normalised and written as the output on the last ring
 //    step).
-//  * The visiting block streams through two LDS buffers in 64-key tiles: K and
-//    V row-major, the 16-byte units of each row XOR-swizzled so
-//    both read patterns below are free of bank conflicts, filled straight from
-//    global memory by buffer_load ... lds while the other buffer is in use.
+//  * The visiting block streams through two LDS buffers in 64-key tiles (32
+//    at d = 256): K and V row-major, the 16-byte units of each row
+//    XOR-swizzled (d = 256: rows padded) so both read patterns below are free
+//    of bank conflicts, filled straight from global memory by
+//    buffer_load ... lds while the other buffer is in use.
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //    in the accumulator layout a lane then holds 16 scores of ONE query row
 //    (lane % 32) and the other 16 of the 32 keys sit in lane ^ 32, so the row
@@ -70,10 +72,36 @@ constexpr float kLazy = 8.0f;
 constexpr float kRefSum = 256.0f;  // 2^kLazy
 constexpr float kRefRaise = 3.0f;  // kLazy - 5
 
-// Keys per LDS tile.
-constexpr int kTileKeys = 64;
 // Matrix products by which an LDS operand read runs ahead of its use.
 constexpr int kReadAhead = 2;
+
+// LDS layout of one K/V tile (K region, then V region; two such buffers).
+//  * d = 64, 128: 64-key tiles, rows of d elements, the 16-byte units of each
+//    row XOR-swizzled (swz); every read pattern is conflict-free and each
+//    operand read has its own per-lane offset.
+//  * d = 256: 32-key tiles (the o accumulators and Q of 32 rows take 192
+//    registers, so the scores of one 32-key block are all that fit beside
+//    them), rows padded instead of swizzled: a K row is 33 units, so a
+//    16-lane group of a K read (16 rows, one unit each) meets 16 bank groups;
+//    a V row is 36 units (four units of padding shift each row by a quarter
+//    of the 64 banks), so the 32 lanes of a transposed V read (4 rows x 4
+//    units x 2 halves) meet all 64 banks once.  Every operand read of a wave
+//    is then one per-lane address plus an immediate offset, which keeps the
+//    kernel within 256 registers.
+//  Tiles are filled in whole 1 KB chunks (64 lanes x 16 bytes); in the padded
+//  layout the lanes that land on padding, or past the last row, fetch a copy
+//  of a valid unit.
+template <int D>
+struct TileLayout {
+  static constexpr bool kPad = D == 256;
+  static constexpr int kKeys = kPad ? 32 : 64;
+  static constexpr int kKRow = kPad ? D + 8 : D;   // K row stride (elements)
+  static constexpr int kVRow = kPad ? D + 32 : D;  // V row stride (elements)
+  static constexpr int kKChunks = (kKeys * kKRow + 511) / 512;
+  static constexpr int kVChunks = (kKeys * kVRow + 511) / 512;
+  static constexpr int kKElems = kKChunks * 512;
+  static constexpr int kBufElems = kKElems + kVChunks * 512;
+};
 
 // ---------------------------------------------------------------------------
 // Per tile: wait for it, request the next one into the other buffer, scores,
@@ -86,17 +114,21 @@ constexpr int kReadAhead = 2;
 template <int D, int NW, bool REF>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void fold_bf16_kernel(const FoldParams p) {
+  using L = TileLayout<D>;
   constexpr int G = 1;  // query groups of 32 rows per wave
-  constexpr int TK = kTileKeys;
+  constexpr int TK = L::kKeys;
   constexpr int NKB = TK / 32;
   constexpr int NC = D / 16;
   constexpr int NDB = D / 32;
   constexpr int UPR = D / 8;
-  constexpr int TE = TK * D;
-  constexpr int CPW = TE / 512 / NW;
+  // 1 KB chunks each wave fills per tile and tensor: chunk wave + NW j (a
+  // wave-uniform test skips those past the last); unpadded tiles split evenly.
+  constexpr int KPW = (L::kKChunks + NW - 1) / NW;
+  constexpr int VPW = (L::kVChunks + NW - 1) / NW;
   constexpr int QT = NW * 32 * G;  // query rows per workgroup
-  static_assert(CPW >= 1 && TE % (512 * NW) == 0, "tile must split into whole 1 KB chunks per wave");
-  __shared__ __attribute__((aligned(1024))) __bf16 lds[2 * 2 * TE];
+  static_assert(L::kPad || (L::kKChunks % NW == 0 && L::kVChunks % NW == 0),
+                "unpadded tiles split into whole 1 KB chunks per wave");
+  __shared__ __attribute__((aligned(1024))) __bf16 lds[2 * L::kBufElems];
 
   // The launch-wide arguments every path reads, loaded here in one round of
   // scalar loads: left to itself the compiler loads each at its first use,
@@ -208,56 +240,123 @@ void fold_bf16_kernel(const FoldParams p) {
   const float c2 = p.scale_log2;
 
   // Direct loads: chunk c of a tile is LDS units [64c, 64c + 64); lane i
-  // writes unit 64c + i = (row, pos) and fetches global unit pos ^ swz(row).
+  // writes unit 64c + i, the (row, unit) of the tile that LDS unit holds.
+  // Unpadded: unit u of row r sits at u ^ swz(r); padded: rows of kKRow / 8
+  // (K) or kVRow / 8 (V) units, the units past D / 8 and the rows past the
+  // tile fetch unit D / 8 - 1 of the last row they reach.
   const int k_sr = (int)p.k_sr, v_sr = (int)p.v_sr;
-  int ld_koff[CPW], ld_voff[CPW];  // byte offsets inside a tile
+  auto chunk = [&](int j) { return L::kPad ? wave + NW * j : wave * KPW + j; };
+  auto k_chunk_ok = [&](int j) { return !L::kPad || chunk(j) < L::kKChunks; };
+  auto v_chunk_ok = [&](int j) { return !L::kPad || chunk(j) < L::kVChunks; };
+  auto unit_src = [&](int c, int ln, int row_units, int& row, int& col) {
+    const int u = c * 64 + ln;
+    if constexpr (L::kPad) {
+      row = min(u / row_units, TK - 1);
+      col = min(u % row_units, UPR - 1);
+    } else {
+      row = u / UPR;
+      col = (u % UPR) ^ swz<D>(row);
+    }
+  };
+  // A copy of the lane id the compiler cannot see through: what is computed
+  // from it is computed where it is used, not hoisted out of the tile loop
+  // into registers held for the whole launch.
+  auto opaque_lane = [&]() {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    return ln;
+  };
+  // Byte offsets inside a tile: chunks j < KRES (VRES) of a wave keep theirs
+  // in registers; the padded layout's last chunks, which only the first waves
+  // fill, compute theirs when issued.
+  constexpr int KRES = L::kPad ? L::kKChunks / NW : KPW;
+  constexpr int VRES = L::kPad ? L::kVChunks / NW : VPW;
+  static_assert(KRES >= 1 && VRES >= 1, "every wave fills a chunk of each tile");
+  int ld_koff[KRES], ld_voff[VRES];
 #pragma unroll
-  for (int j = 0; j < CPW; ++j) {
-    const int u = (wave * CPW + j) * 64 + lane;
-    const int lrow = u / UPR;
-    const int gunit = (u % UPR) ^ swz<D>(lrow);
-    ld_koff[j] = (lrow * k_sr + gunit * 8) * 2;
-    ld_voff[j] = (lrow * v_sr + gunit * 8) * 2;
+  for (int j = 0; j < (KRES > VRES ? KRES : VRES); ++j) {
+    int row, col;
+    if (j < KRES) {
+      unit_src(chunk(j), lane, L::kKRow / 8, row, col);
+      ld_koff[j] = (row * k_sr + col * 8) * 2;
+    }
+    if (j < VRES) {
+      if constexpr (L::kPad) unit_src(chunk(j), lane, L::kVRow / 8, row, col);
+      ld_voff[j] = (row * v_sr + col * 8) * 2;
+    }
   }
+  auto koff = [&](int j) {
+    if (j < KRES) return ld_koff[j < KRES ? j : 0];
+    int row, col;
+    unit_src(chunk(j), opaque_lane(), L::kKRow / 8, row, col);
+    return (row * k_sr + col * 8) * 2;
+  };
+  auto voff = [&](int j) {
+    if (j < VRES) return ld_voff[j < VRES ? j : 0];
+    int row, col;
+    unit_src(chunk(j), opaque_lane(), L::kVRow / 8, row, col);
+    return (row * v_sr + col * 8) * 2;
+  };
   auto issue_tile = [&](int kt, int buf) {
     const int key0 = kt * TK;
-    __bf16* kl = lds + buf * 2 * TE + wave * CPW * 512;
-    __bf16* vl = kl + TE;
+    __bf16* kl = lds + buf * L::kBufElems;
+    __bf16* vl = kl + L::kKElems;
     if (key0 + TK <= kv_len) {
       const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + (int64_t)key0 * k_sr);
       const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + (int64_t)key0 * v_sr);
 #pragma unroll
-      for (int j = 0; j < CPW; ++j) {
-        bload_lds16(kr, ld_koff[j], kl + j * 512);
-        bload_lds16(vr, ld_voff[j], vl + j * 512);
-      }
-    } else {  // ragged last tile: rows past the end re-read the last row
+      for (int j = 0; j < KPW; ++j)
+        if (k_chunk_ok(j)) bload_lds16(kr, koff(j), kl + chunk(j) * 512);
 #pragma unroll
-      for (int j = 0; j < CPW; ++j) {
-        const int u = (wave * CPW + j) * 64 + lane;
-        const int lrow = u / UPR;
-        const int gunit = (u % UPR) ^ swz<D>(lrow);
-        const int64_t g = min(key0 + lrow, kv_len - 1);
-        gload_lds16(kbase + g * k_sr + gunit * 8, kl + j * 512);
-        gload_lds16(vbase + g * v_sr + gunit * 8, vl + j * 512);
-      }
+      for (int j = 0; j < VPW; ++j)
+        if (v_chunk_ok(j)) bload_lds16(vr, voff(j), vl + chunk(j) * 512);
+    } else {  // ragged last tile: rows past the end re-read the last row
+      const int ln = L::kPad ? opaque_lane() : lane;
+#pragma unroll
+      for (int j = 0; j < KPW; ++j)
+        if (k_chunk_ok(j)) {
+          int row, col;
+          unit_src(chunk(j), ln, L::kKRow / 8, row, col);
+          const int64_t g = min(key0 + row, kv_len - 1);
+          gload_lds16(kbase + g * k_sr + col * 8, kl + chunk(j) * 512);
+        }
+#pragma unroll
+      for (int j = 0; j < VPW; ++j)
+        if (v_chunk_ok(j)) {
+          int row, col;
+          unit_src(chunk(j), ln, L::kVRow / 8, row, col);
+          const int64_t g = min(key0 + row, kv_len - 1);
+          gload_lds16(vbase + g * v_sr + col * 8, vl + chunk(j) * 512);
+        }
     }
   };
 
-  const int gk = lg ^ swz<D>(lr);
-  int k_rd[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) k_rd[c] = lr * D + (((2 * c) ^ gk) << 3);
+  // Operand read offsets (elements).  K: row lr, unit 2 c + lg for d chunk c.
+  // V^T (two transposed 8-byte reads per operand, 4 keys x 4 units x 2 halves
+  // per 32 lanes): key vr + 8 run, unit 4 db + vx, half lane & 1.
   const int vr = 4 * lg + ((lane & 15) >> 2);
   const int vx = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-  int v_rd[2][NDB];
+  constexpr int NKO = L::kPad ? 1 : NC;
+  constexpr int NVO = L::kPad ? 1 : NDB;
+  int k_rd[NKO];
+  int v_rd[2][NVO];
+  if constexpr (L::kPad) {
+    k_rd[0] = lr * L::kKRow + 8 * lg;
+    v_rd[0][0] = vr * L::kVRow + 8 * vx + 4 * (lane & 1);
+  } else {
+    const int gk = lg ^ swz<D>(lr);
 #pragma unroll
-  for (int run = 0; run < 2; ++run) {
-    const int rr = vr + 8 * run;
-    const int y = vx ^ swz<D>(rr);
+    for (int c = 0; c < NC; ++c) k_rd[c] = lr * D + (((2 * c) ^ gk) << 3);
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) v_rd[run][db] = rr * D + (((4 * db) ^ y) << 3) + 4 * (lane & 1);
+    for (int run = 0; run < 2; ++run) {
+      const int rr = vr + 8 * run;
+      const int y = vx ^ swz<D>(rr);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) v_rd[run][db] = rr * D + (((4 * db) ^ y) << 3) + 4 * (lane & 1);
+    }
   }
+  auto k_at = [&](int c) { return L::kPad ? k_rd[0] + 16 * c : k_rd[c]; };
+  auto v_at = [&](int run, int db) { return L::kPad ? v_rd[0][0] + 8 * L::kVRow * run + 32 * db : v_rd[run][db]; };
 
   // S^T of group g against the K tile at kl; the 32-key blocks are
   // independent accumulation chains, interleaved.  The products are issued in
@@ -267,7 +366,7 @@ void fold_bf16_kernel(const FoldParams p) {
   auto scores = [&](f32x16 (&s)[NKB], const __bf16* kl, int g) {
     constexpr int N = NC * NKB;
     auto rd = [&](int i) {  // product i: d chunk i / NKB, key block i % NKB
-      return *(const bf16x8*)(kl + 32 * (i % NKB) * D + k_rd[i / NKB]);
+      return *(const bf16x8*)(kl + 32 * (i % NKB) * L::kKRow + k_at(i / NKB));
     };
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
@@ -369,9 +468,9 @@ void fold_bf16_kernel(const FoldParams p) {
       b[h] = __builtin_bit_cast(bf16x8, u32x4{pk[kb][4 * c], pk[kb][4 * c + 1], pk[kb][4 * c + 2], pk[kb][4 * c + 3]});
     }
     auto rd = [&](int i) {  // product i: key run pair i / NDB, d block i % NDB
-      const __bf16* vrow = vl + 16 * (i / NDB) * D;
-      const u32x2 w0 = __builtin_bit_cast(u32x2, lds_tr16(vrow + v_rd[0][i % NDB]));
-      const u32x2 w1 = __builtin_bit_cast(u32x2, lds_tr16(vrow + v_rd[1][i % NDB]));
+      const __bf16* vrow = vl + 16 * (i / NDB) * L::kVRow;
+      const u32x2 w0 = __builtin_bit_cast(u32x2, lds_tr16(vrow + v_at(0, i % NDB)));
+      const u32x2 w1 = __builtin_bit_cast(u32x2, lds_tr16(vrow + v_at(1, i % NDB)));
       return __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w1[0], w1[1]});
     };
     bf16x8 a[kReadAhead];
@@ -390,8 +489,8 @@ void fold_bf16_kernel(const FoldParams p) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile kt landed for this wave
     __syncthreads();                     // ... for every wave; the other buffer is free
     if (kt + 1 < n_kt) issue_tile(kt + 1, buf ^ 1);
-    const __bf16* kc = lds + buf * 2 * TE;
-    const __bf16* vc = kc + TE;
+    const __bf16* kc = lds + buf * L::kBufElems;
+    const __bf16* vc = kc + L::kKElems;
     f32x16 sa[NKB];
     unsigned pa[NKB][8];
     scores(sa, kc, 0);
@@ -481,7 +580,6 @@ void fold_bf16_kernel(const FoldParams p) {
 constexpr int waves_for(int d) { return d == 128 ? 8 : 4; }
 
 hipError_t launch_fold_bf16(const FoldParams& p, int d, hipStream_t s) {
-  if (d == 256) return launch_fold_bf16_r16(p, d, s);
   const int rows_per_wg = waves_for(d) * 32;
   const int64_t tiles_q = (p.q_rows + rows_per_wg - 1) / rows_per_wg;
   const int64_t grid = tiles_q * p.n_res * p.H * p.B;
@@ -501,6 +599,12 @@ hipError_t launch_fold_bf16(const FoldParams& p, int d, hipStream_t s) {
         fold_bf16_kernel<128, waves_for(128), true><<<gd, bd, 0, s>>>(p);
       else
         fold_bf16_kernel<128, waves_for(128), false><<<gd, bd, 0, s>>>(p);
+      break;
+    case 256:
+      if (ref)
+        fold_bf16_kernel<256, waves_for(256), true><<<gd, bd, 0, s>>>(p);
+      else
+        fold_bf16_kernel<256, waves_for(256), false><<<gd, bd, 0, s>>>(p);
       break;
     default:
       return hipErrorInvalidValue;

@@ -152,8 +152,6 @@ struct BwdParams {
 
 // Each launcher returns the launch status (hipGetLastError after the launch).
 hipError_t launch_fold_bf16(const FoldParams& p, int d, hipStream_t s);
-// The 16-rows-per-wave kernel for wide heads (d = 256); launch_fold_bf16 routes to it.
-hipError_t launch_fold_bf16_r16(const FoldParams& p, int d, hipStream_t s);
 hipError_t launch_fold_f32(const FoldParams& p, int d, hipStream_t s);
 hipError_t launch_state_init(float* m, float* l, float* o, int64_t rows_total, int d, hipStream_t s);
 hipError_t launch_bwd_dq_bf16(const BwdParams& p, int d, hipStream_t s);

@@ -82,21 +82,24 @@ def test_traffic_is_dropped_when_the_source_changes(tmp_path, monkeypatch):
     assert bench._traffic("ring-128k-P16", "bf16", backward=True) is None
 
 
-def test_d256_traffic_is_tied_to_its_own_kernel_source(tmp_path, monkeypatch):
-    """The d = 256 fold runs the 16-row kernel of fold_bf16_r16.hip: its traffic
-    entry is gated on that file's hash, not on the d = 64/128 kernel's file."""
+def test_d256_traffic_is_tied_to_the_fold_kernel_source(tmp_path, monkeypatch):
+    """Every bf16 head dim (d = 64, 128, 256) runs fold_bf16_kernel of
+    fold_bf16.hip: a d = 256 traffic entry is gated on that file's hash and
+    turns null once the file changes."""
     import hashlib
 
-    src = os.path.join(bench.ROOT, "blockwise_online_softmax_fold_amd", "csrc", "fold_bf16_r16.hip")
+    src = os.path.join(bench.ROOT, "blockwise_online_softmax_fold_amd", "csrc", "fold_bf16.hip")
     with open(src, "rb") as f:
         want = hashlib.sha256(f.read()).hexdigest()[:16]
     assert bench._source_hash("bf16", False, 256) == want
-    assert bench._source_hash("bf16", False, 256) != bench._source_hash("bf16", False, 128)
+    assert bench._source_hash("bf16", False, 256) == bench._source_hash("bf16", False, 128)
+    assert bench._source_hash("bf16", False, 256) != bench._source_hash("f32", False, 256)
     path = tmp_path / "traffic.json"
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(path))
     path.write_text(json.dumps({"w5": {"hbm_bytes_per_launch": 5.0, "source_sha256_16": want}}))
     assert bench._traffic("w5", "bf16", False, 256) == 5.0
-    assert bench._traffic("w5", "bf16", False, 128) is None
+    path.write_text(json.dumps({"w5": {"hbm_bytes_per_launch": 5.0, "source_sha256_16": "0" * 16}}))
+    assert bench._traffic("w5", "bf16", False, 256) is None
 
 
 def test_more_than_one_gpu_is_refused():

@@ -110,10 +110,11 @@ def test_fold_block_state_per_step(ra, dtype, d, q_rows, kv_rows):
         check_output(to64(o) / to64(l)[..., None], r.o / r.l[..., None], dtype, f"step {t} o/l")
 
 
-# Visiting-block lengths that take every path of the d = 256 kernel's tile loop
-# (32-key tiles through a three-deep LDS ring): a lone ragged tile, one full
-# tile, a full tile plus a ragged one, the groups of three full tiles, the
-# one-by-one remainder, and a ragged last tile after either.
+# Visiting-block lengths that take every path of the d = 256 tile loop (32-key
+# tiles in padded LDS rows, two buffers, full tiles two per loop iteration): a
+# lone ragged tile, one full tile, a full tile plus a ragged one, whole pairs,
+# a pair plus a single full tile, and a ragged last tile after either; 130
+# query rows leave the second 128-row workgroup two rows.
 @pytest.mark.parametrize("kv_rows", [31, 32, 33, 64, 95, 96, 97, 128, 161, 224, 225])
 def test_fold_block_d256_tile_ring(ra, kv_rows):
     _say(f"fold_block d=256 q_rows=130 kv_rows={kv_rows} seed=11")
