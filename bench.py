@@ -25,7 +25,9 @@ steps.  --device-sweep instead times one device's ring step at its real shape
 d128 bf16) for several b, next to the time one K/V block of that size takes
 over one xGMI link, and prints one JSON line with a row per b.  `clock` is the shader clock the driver reported while the timed steps
 ran (sampled from pp_dpm_sclk by a host thread) and the step throughput as a
-share of the peak scaled to that clock (null where the file is not readable).
+share of the peak scaled to that clock (null where the file is not readable);
+`clock.power` is the socket power sampled beside it (hwmon power1_input) with
+the board's cap (power1_cap).
 """
 
 from __future__ import annotations
@@ -252,8 +254,9 @@ def cpu_baseline(w, q, k, v, seconds: float, out=None) -> dict:
 
 class ClockSampler:
     """Samples the shader clock the driver reports (the starred level of
-    pp_dpm_sclk, in MHz) from a host thread while the timed steps run; reads
-    a sysfs file only, never the GPU."""
+    pp_dpm_sclk, in MHz) and the socket power (hwmon power1_input, in W, with
+    the board's power1_cap) from a host thread while the timed steps run;
+    reads sysfs files only, never the GPU."""
 
     def __init__(self, period_s: float = 0.02):
         import glob
@@ -261,8 +264,12 @@ class ClockSampler:
 
         paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
         self.path = paths[0] if paths else None
+        hw = sorted(glob.glob(os.path.join(os.path.dirname(self.path), "hwmon", "hwmon*"))) if self.path else []
+        self.power_path = os.path.join(hw[0], "power1_input") if hw else None
+        self.cap_w = _read_watts(os.path.join(hw[0], "power1_cap")) if hw else None
         self.period = period_s
         self.samples: list[float] = []
+        self.watts: list[float] = []
         self._stop = threading.Event()
         self._thread = threading.Thread(target=self._run, daemon=True)
 
@@ -281,6 +288,9 @@ class ClockSampler:
             mhz = self._read()
             if mhz is not None:
                 self.samples.append(mhz)
+            w = _read_watts(self.power_path)
+            if w is not None:
+                self.watts.append(w)
             self._stop.wait(self.period)
 
     def __enter__(self):
@@ -299,9 +309,25 @@ class ClockSampler:
         med = float(sorted(self.samples)[len(self.samples) // 2])
         # the published peak holds at the 2.4 GHz maximum shader clock
         at_clock = peak * med / 2400.0
-        return {"source": "pp_dpm_sclk", "median_mhz": med, "min_mhz": min(self.samples),
-                "max_mhz": max(self.samples), "samples": len(self.samples),
-                "peak_at_clock": round(at_clock, 1), "pct_peak_at_clock": round(100.0 * value / at_clock, 2)}
+        rec = {"source": "pp_dpm_sclk", "median_mhz": med, "min_mhz": min(self.samples),
+               "max_mhz": max(self.samples), "samples": len(self.samples),
+               "peak_at_clock": round(at_clock, 1), "pct_peak_at_clock": round(100.0 * value / at_clock, 2)}
+        if self.watts:
+            w = sorted(self.watts)
+            rec["power"] = {"source": "hwmon power1_input", "median_w": round(w[len(w) // 2], 1),
+                            "max_w": round(w[-1], 1), "cap_w": self.cap_w, "samples": len(w)}
+        return rec
+
+
+def _read_watts(path):
+    """A hwmon power file (microwatts) in watts, or None."""
+    if path is None:
+        return None
+    try:
+        with open(path) as f:
+            return int(f.read().strip()) / 1e6
+    except (OSError, ValueError):
+        return None
 
 
 XGMI_LINK_GBPS = 153.0  # one MI355X xGMI link, one direction (GB/s)

@@ -144,3 +144,27 @@ def test_parity_figures_apply_the_bars():
     assert not bench.parity_figures(bad, ref, "bf16")["within_bar"]
     assert bench.parity_figures(ref * (1 + 5e-6), ref, "f32")["within_bar"]
     assert not bench.parity_figures(ref * (1 + 5e-5), ref, "f32")["within_bar"]
+
+
+def test_clock_sampler_reads_sysfs_clock_and_power(tmp_path, monkeypatch):
+    """The sampler takes the starred pp_dpm_sclk level as the clock and
+    hwmon power1_input / power1_cap (microwatts) as watts."""
+    dev = tmp_path / "card0" / "device"
+    hw = dev / "hwmon" / "hwmon0"
+    hw.mkdir(parents=True)
+    (dev / "pp_dpm_sclk").write_text("0: 500Mhz\n1: 1900Mhz *\n2: 2400Mhz\n")
+    (hw / "power1_input").write_text("1395000000\n")
+    (hw / "power1_cap").write_text("1400000000\n")
+    import glob as _glob
+
+    real_glob = _glob.glob
+    monkeypatch.setattr(_glob, "glob", lambda pat, *a, **k: [str(dev / "pp_dpm_sclk")] if pat.endswith("pp_dpm_sclk")
+                        else real_glob(pat, *a, **k))
+    c = bench.ClockSampler()
+    assert c.cap_w == 1400.0
+    c.samples.append(c._read())
+    c.watts.append(bench._read_watts(c.power_path))
+    rec = c.summary(950.0, 2500.0)
+    assert rec["median_mhz"] == 1900.0
+    assert rec["peak_at_clock"] == round(2500.0 * 1900.0 / 2400.0, 1)
+    assert rec["power"]["median_w"] == 1395.0 and rec["power"]["cap_w"] == 1400.0
