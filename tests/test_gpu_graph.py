@@ -42,7 +42,9 @@ def _eager_noise():
 
 @pytest.mark.parametrize("dtype,N,P,d,layout", [(torch.float32, 1024, 4, 64, None),
                                                  (torch.bfloat16, 2048, 4, 128, None),
-                                                 (torch.bfloat16, 1536, 3, 128, "zigzag")])
+                                                 (torch.bfloat16, 1536, 3, 128, "zigzag"),
+                                                 (torch.bfloat16, 1040, 4, 256, None),
+                                                 (torch.bfloat16, 768, 3, 256, "striped")])
 def test_ring_forward_graph_replay(ra, dtype, N, P, d, layout):
     _say(f"graph replay ring forward dtype={dtype} N={N} P={P} d={d} layout={layout}")
     q, k, v = _inputs(1, 2, N, d, dtype, 7 + N)
