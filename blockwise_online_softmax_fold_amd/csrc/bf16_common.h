@@ -1,6 +1,7 @@
 // gfx950 device helpers shared by the bf16 fold kernels (forward and
 // backward): vector types, XCD-aware workgroup order, lane-pair reductions,
-// bf16 packing, LDS transpose reads, the LDS swizzle and direct-to-LDS loads.
+// bf16 packing, LDS transpose reads, the LDS swizzle, direct-to-LDS loads and
+// the LDS barrier.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -79,26 +80,46 @@ __device__ __forceinline__ int swz(int r) {
     return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
-// 16 bytes from global memory straight into LDS (global_load_lds_dwordx4):
-// lane i's bytes land at lds_wave_base + 16 i.
-__device__ __forceinline__ void gload_lds16(const __bf16* g, __bf16* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(g),
-                                   (__attribute__((address_space(3))) void*)(lds_wave_base), 16, 0, 0);
+// Direct-to-LDS loads, issued from inline assembly so that the compiler does
+// not track them: it neither counts them in its own vmcnt waits nor makes
+// later LDS reads wait for them (it cannot tell which LDS bytes such a load
+// writes, and so made the value product of every other tile wait for the
+// next tile's loads).  The tile loops wait for them themselves (s_waitcnt
+// vmcnt, then lds_barrier), and wait for every load issued before a loop
+// once before it.  M0 is an operand of the statement, so the compiler writes
+// it and knows it is taken; the s_nop is the wait state between an SALU write
+// of M0 and the load that reads it.  Lane l's bytes land at LDS address
+// lds + 16 l (lds + 4 l for the dword form).
+//  * global_load_lds_dwordx4 / _dword from a 64-bit address per lane;
+//  * buffer_load_dwordx4 ... lds from byte offset voff of the buffer whose
+//    resource words are rs (the 64-bit base in scalar registers, so a tile
+//    costs no vector address arithmetic).
+__device__ __forceinline__ void gload_lds16(const void* g, unsigned lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "{m0}"(lds) : "memory");
 }
-
-// Buffer resource over `base` with no effective range limit (every access is
-// computed in bounds by the kernel) for the raw buffer loads below.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
+__device__ __forceinline__ void gload_lds4(const void* g, unsigned lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" : : "v"(g), "{m0}"(lds) : "memory");
 }
-
-// 16 bytes at byte offset voff of the buffer straight into LDS
-// (buffer_load_dwordx4 ... lds): lane i's bytes land at lds_wave_base + 16 i.
-// The 64-bit base lives in scalar registers, so a tile costs no vector
-// address arithmetic.
-__device__ __forceinline__ void bload_lds16(__amdgpu_buffer_rsrc_t rs, int voff, __bf16* lds_wave_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(lds_wave_base), 16, voff, 0,
-                                           0, 0);
+__device__ __forceinline__ void bload_lds16(u32x4 rs, int voff, unsigned lds) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(rs), "{m0}"(lds) : "memory");
+}
+// The LDS address of a __shared__ object.
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(size_t)(const __attribute__((address_space(3))) void*)p;
+}
+// Resource words of a buffer over `base` with no effective range limit (every
+// access is computed in bounds by the kernel).
+__device__ __forceinline__ u32x4 rsrc_words(const void* base) {
+  const size_t a = (size_t)base;
+  return u32x4{(unsigned)a, (unsigned)(a >> 32) & 0xffffu, 0x7fffffffu, 0x00020000u};
+}
+// Workgroup barrier that orders LDS only: the tile loops call it right after
+// their own vmcnt wait, with no global access of theirs left to order
+// (__syncthreads would add a wait for every vector memory access in flight).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 }  // namespace dev

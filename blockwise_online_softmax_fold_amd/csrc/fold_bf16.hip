@@ -60,32 +60,6 @@ namespace {
 
 using namespace dev;
 
-// 16 bytes of global memory per lane straight into LDS, issued from inline
-// assembly so that the compiler does not track the load: it neither counts it
-// in its own vmcnt waits nor makes later LDS reads wait for it (it cannot tell
-// which LDS bytes such a load writes); the tile loop waits for it itself.  M0
-// is an operand of the statement, so the compiler writes it and knows it is
-// taken; the s_nop is the wait state between an SALU write of M0 and the load
-// that reads it.  Lane l's bytes land at LDS address lds + 16 l.
-//  * global_load_lds_dwordx4 from a 64-bit address per lane;
-//  * buffer_load_dwordx4 ... lds from byte offset voff of the buffer whose
-//    resource words are rs.
-__device__ __forceinline__ void gload_lds16_asm(const void* g, unsigned lds) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "{m0}"(lds) : "memory");
-}
-__device__ __forceinline__ void bload_lds16_asm(u32x4 rs, int voff, unsigned lds) {
-  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(rs), "{m0}"(lds) : "memory");
-}
-__device__ __forceinline__ unsigned lds_addr(const void* p) {
-  return (unsigned)(size_t)(const __attribute__((address_space(3))) void*)p;
-}
-// Resource words of a buffer over `base` with no effective range limit (the
-// kernel computes every access in bounds).
-__device__ __forceinline__ u32x4 rsrc_words(const void* base) {
-  const size_t a = (size_t)base;
-  return u32x4{(unsigned)a, (unsigned)(a >> 32) & 0xffffu, 0x7fffffffu, 0x00020000u};
-}
-
 // Lazy rescaling threshold (base-2 units): weights stay below 2^kLazy.
 constexpr float kLazy = 8.0f;
 // With the reference state (kRefState), a tile's weights are first taken
@@ -155,11 +129,6 @@ void fold_bf16_kernel(const FoldParams p) {
   static_assert(L::kPad || (L::kKChunks % NW == 0 && L::kVChunks % NW == 0),
                 "unpadded tiles split into whole 1 KB chunks per wave");
   __shared__ __attribute__((aligned(1024))) __bf16 lds[2 * L::kBufElems];
-  // d = 128: tile loads from inline assembly and a barrier that orders LDS
-  // only (measured 2-3 % faster per fold than compiler-tracked loads, whose
-  // waits also stall the value product of every other tile on the next
-  // tile's loads).
-  constexpr bool kAsmLoads = D == 128;
 
   // The launch-wide arguments every path reads, loaded here in one round of
   // scalar loads: left to itself the compiler loads each at its first use,
@@ -332,22 +301,15 @@ void fold_bf16_kernel(const FoldParams p) {
     const int key0 = kt * TK;
     __bf16* kl = lds + buf * L::kBufElems;
     __bf16* vl = kl + L::kKElems;
-    if (kAsmLoads && key0 + TK <= kv_len) {
+    if (key0 + TK <= kv_len) {
       const u32x4 kr = rsrc_words(kbase + (int64_t)key0 * k_sr);
       const u32x4 vr = rsrc_words(vbase + (int64_t)key0 * v_sr);
 #pragma unroll
-      for (int j = 0; j < KPW; ++j) bload_lds16_asm(kr, koff(j), lds_addr(kl + chunk(j) * 512));
-#pragma unroll
-      for (int j = 0; j < VPW; ++j) bload_lds16_asm(vr, voff(j), lds_addr(vl + chunk(j) * 512));
-    } else if (key0 + TK <= kv_len) {
-      const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + (int64_t)key0 * k_sr);
-      const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + (int64_t)key0 * v_sr);
-#pragma unroll
       for (int j = 0; j < KPW; ++j)
-        if (k_chunk_ok(j)) bload_lds16(kr, koff(j), kl + chunk(j) * 512);
+        if (k_chunk_ok(j)) bload_lds16(kr, koff(j), lds_addr(kl + chunk(j) * 512));
 #pragma unroll
       for (int j = 0; j < VPW; ++j)
-        if (v_chunk_ok(j)) bload_lds16(vr, voff(j), vl + chunk(j) * 512);
+        if (v_chunk_ok(j)) bload_lds16(vr, voff(j), lds_addr(vl + chunk(j) * 512));
     } else {  // ragged last tile: rows past the end re-read the last row
       const int ln = L::kPad ? opaque_lane() : lane;
 #pragma unroll
@@ -356,10 +318,7 @@ void fold_bf16_kernel(const FoldParams p) {
           int row, col;
           unit_src(chunk(j), ln, L::kKRow / 8, row, col);
           const int64_t g = min(key0 + row, kv_len - 1);
-          if constexpr (kAsmLoads)
-            gload_lds16_asm(kbase + g * k_sr + col * 8, lds_addr(kl + chunk(j) * 512));
-          else
-            gload_lds16(kbase + g * k_sr + col * 8, kl + chunk(j) * 512);
+          gload_lds16(kbase + g * k_sr + col * 8, lds_addr(kl + chunk(j) * 512));
         }
 #pragma unroll
       for (int j = 0; j < VPW; ++j)
@@ -367,10 +326,7 @@ void fold_bf16_kernel(const FoldParams p) {
           int row, col;
           unit_src(chunk(j), ln, L::kVRow / 8, row, col);
           const int64_t g = min(key0 + row, kv_len - 1);
-          if constexpr (kAsmLoads)
-            gload_lds16_asm(vbase + g * v_sr + col * 8, lds_addr(vl + chunk(j) * 512));
-          else
-            gload_lds16(vbase + g * v_sr + col * 8, vl + chunk(j) * 512);
+          gload_lds16(vbase + g * v_sr + col * 8, lds_addr(vl + chunk(j) * 512));
         }
     }
   };
@@ -531,15 +487,7 @@ void fold_bf16_kernel(const FoldParams p) {
   // One tile whose K/V sit in LDS buffer `buf`; `masked` applies lim.
   auto tile = [&](int kt, int buf, bool masked) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile kt landed for this wave
-    if constexpr (kAsmLoads) {
-      // ... for every wave; the other buffer is free.  The fences order LDS
-      // only: no global access is in flight here.
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-    } else {
-      __syncthreads();  // ... for every wave; the other buffer is free
-    }
+    lds_barrier();                       // ... for every wave; the other buffer is free
     if (kt + 1 < n_kt) issue_tile(kt + 1, buf ^ 1);
     const __bf16* kc = lds + buf * L::kBufElems;
     const __bf16* vc = kc + L::kKElems;
@@ -570,7 +518,7 @@ void fold_bf16_kernel(const FoldParams p) {
     // Q, the state and tile 0 in registers and LDS before the loop: with the
     // tile loads out of its sight, the compiler would otherwise wait for Q at
     // its first use, inside the loop, on every tile.
-    if constexpr (kAsmLoads) __builtin_amdgcn_s_waitcnt(0x0F70);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     int kt = 0;
     for (; kt + 2 <= n_plain; kt += 2) {
       tile(kt, 0, false);

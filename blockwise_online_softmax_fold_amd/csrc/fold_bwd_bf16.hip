@@ -75,9 +75,9 @@ __device__ __forceinline__ void issue_rows(const __bf16* base, int sr, const int
   constexpr int UPR = D / 8;
   __bf16* dst = tile + wave * CPW * 512;
   if (row0 + R <= n) {
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + (int64_t)row0 * sr);
+    const u32x4 rs = rsrc_words(base + (int64_t)row0 * sr);
 #pragma unroll
-    for (int j = 0; j < CPW; ++j) bload_lds16(rs, off[j], dst + j * 512);
+    for (int j = 0; j < CPW; ++j) bload_lds16(rs, off[j], lds_addr(dst + j * 512));
   } else {
 #pragma unroll
     for (int j = 0; j < CPW; ++j) {
@@ -85,7 +85,7 @@ __device__ __forceinline__ void issue_rows(const __bf16* base, int sr, const int
       const int lrow = u / UPR;
       const int gunit = (u % UPR) ^ swz<D>(lrow);
       const int64_t g = min(row0 + lrow, n - 1);
-      gload_lds16(base + g * sr + gunit * 8, dst + j * 512);
+      gload_lds16(base + g * sr + gunit * 8, lds_addr(dst + j * 512));
     }
   }
 }
@@ -225,7 +225,7 @@ void bwd_dq_kernel(const BwdParams p) {
 
   auto tile = [&](int kt, int buf, bool masked) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile kt landed for this wave
-    __syncthreads();                     // ... for every wave; the other buffer is free
+    lds_barrier();                       // ... for every wave; the other buffer is free
     if (kt + 1 < n_kt) issue_tile(kt + 1, buf ^ 1);
     const __bf16* kl = lds + buf * 2 * TE;
     const __bf16* vl = kl + TE;
@@ -280,6 +280,7 @@ void bwd_dq_kernel(const BwdParams p) {
 
   if (n_kt > 0) {
     issue_tile(0, 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // Q, dO, the row statistics and tile 0, before the loop
     int kt = 0;
     for (; kt + 2 <= n_plain; kt += 2) {
       tile(kt, 0, false);
@@ -406,16 +407,17 @@ void bwd_dkdv_kernel(const BwdParams p) {
   int ld_qoff[CPW], ld_doff[CPW];
   tile_offsets<D, CPW>(wave, lane, q_sr, ld_qoff);
   tile_offsets<D, CPW>(wave, lane, do_sr, ld_doff);
+  // nl2 (lanes 0-31) or dd (lanes 32-63) of this lane's row, chosen once here:
+  // chosen inside the loop, the pointer was re-read from the kernel arguments
+  // on every tile.
+  const float* lrow_src = (lg == 0 ? p.nl2 : p.dd) + rbase;
+  asm volatile("" : "+v"(lrow_src));
   auto issue_tile = [&](int qt, int buf) {
     __bf16* ql = lds + buf * 2 * TE;
     issue_rows<D, CPW, TQ>(qbase, q_sr, ld_qoff, qt * TQ, q_len, ql, wave, lane);
     issue_rows<D, CPW, TQ>(dbase, do_sr, ld_doff, qt * TQ, q_len, ql + TE, wave, lane);
-    if (wave == 0) {  // nl2 of the tile's rows into lrow[buf][0, TQ), dd into [TQ, 2 TQ)
-      const int rr = min(qt * TQ + lr, q_len - 1);
-      const float* src = (lg == 0 ? p.nl2 : p.dd) + rbase + rr;
-      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(src),
-                                       (__attribute__((address_space(3))) void*)(&lrow[buf][0]), 4, 0, 0);
-    }
+    if (wave == 0)  // nl2 of the tile's rows into lrow[buf][0, TQ), dd into [TQ, 2 TQ)
+      gload_lds4(lrow_src + min(qt * TQ + lr, q_len - 1), lds_addr(&lrow[buf][0]));
   };
 
   const int gq = lg ^ swz<D>(lr);
@@ -432,7 +434,7 @@ void bwd_dkdv_kernel(const BwdParams p) {
 
   auto tile = [&](int qt, int buf, bool masked) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile qt landed for this wave
-    __syncthreads();                     // ... for every wave; the other buffer is free
+    lds_barrier();                       // ... for every wave; the other buffer is free
     if (qt + 1 < n_qt) issue_tile(qt + 1, buf ^ 1);
     const __bf16* ql = lds + buf * 2 * TE;
     const __bf16* dl = ql + TE;
@@ -527,6 +529,7 @@ void bwd_dkdv_kernel(const BwdParams p) {
         issue_rows<D, CPW, TQ>(vb, v_sr, ld_voff, kt * KT + i * TQ, kv_len, vlds + i * TE, wave, lane);
     }
     issue_tile(qt0, qt0 & 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // K, V, the V rows and tile qt0, before the loop
     for (int qt = qt0; qt < n_qt; ++qt) tile(qt, qt & 1, qt < qt_plain || qt >= n_full);
   }
 

@@ -18,9 +18,9 @@ enum FoldFlags : int {
   // The spilled state is internal to a ring: m may hold the reference maximum
   // the weights were taken against (base 2, at most the running maximum) with
   // l and o relative to it, instead of the running maximum itself.  O and the
-  // log-sum-exp are the same either way.  fold_bf16_kernel (d = 64, 128) keeps
-  // the reference; the other kernels ignore the flag and keep the running
-  // maximum, which is one such state too.
+  // log-sum-exp are the same either way.  fold_bf16_kernel (d = 64, 128, 256)
+  // keeps the reference; the fp32 kernel ignores the flag and keeps the
+  // running maximum, which is one such state too.
   kRefState = 8,
 };
 
