@@ -331,6 +331,41 @@ void fold_bf16_kernel(const FoldParams p) {
     }
   };
 
+  // The ring hand-off fused into the fold (p.send_k set): this workgroup
+  // writes tiles qt, qt + n_qt, qt + 2 n_qt, ... of the visiting block from
+  // LDS to the slot the next ring step reads, the resident's other workgroups
+  // the rest.  LDS unit 64 c + l holds the block's (row, unit) that lane l
+  // loaded into it, so each lane writes its own unit back out (the padded
+  // layout's extra units hold copies and write the same bytes twice).
+  __bf16* const send_k =
+      p.send_k == nullptr ? nullptr : (__bf16*)p.send_k + bi * p.send_sb + hi * p.send_sh + p.send_off[r];
+  __bf16* const send_v =
+      p.send_v == nullptr ? nullptr : (__bf16*)p.send_v + bi * p.send_sb + hi * p.send_sh + p.send_off[r];
+  const int n_qt = (q_len + QT - 1) / QT;
+  int send_at = send_k != nullptr ? qt : 0x7fffffff;  // the next tile this workgroup writes
+  auto send_tile = [&](int kt, int buf) {
+    const int key0 = kt * TK;
+    const __bf16* kl = lds + buf * L::kBufElems;
+    const __bf16* vl = kl + L::kKElems;
+    const int ln = opaque_lane();
+#pragma unroll
+    for (int j = 0; j < KPW; ++j)
+      if (k_chunk_ok(j)) {
+        int row, col;
+        unit_src(chunk(j), ln, L::kKRow / 8, row, col);
+        const bf16x8 x = *(const bf16x8*)(kl + chunk(j) * 512 + 8 * ln);
+        if (key0 + row < kv_len) *(bf16x8*)(send_k + (int64_t)(key0 + row) * D + col * 8) = x;
+      }
+#pragma unroll
+    for (int j = 0; j < VPW; ++j)
+      if (v_chunk_ok(j)) {
+        int row, col;
+        unit_src(chunk(j), ln, L::kVRow / 8, row, col);
+        const bf16x8 x = *(const bf16x8*)(vl + chunk(j) * 512 + 8 * ln);
+        if (key0 + row < kv_len) *(bf16x8*)(send_v + (int64_t)(key0 + row) * D + col * 8) = x;
+      }
+  };
+
   // Operand read offsets (elements).  K: row lr, unit 2 c + lg for d chunk c.
   // V^T (two transposed 8-byte reads per operand, 4 keys x 4 units x 2 halves
   // per 32 lanes): key vr + 8 run, unit 4 db + vx, half lane & 1.
@@ -489,6 +524,10 @@ void fold_bf16_kernel(const FoldParams p) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile kt landed for this wave
     lds_barrier();                       // ... for every wave; the other buffer is free
     if (kt + 1 < n_kt) issue_tile(kt + 1, buf ^ 1);
+    if (kt == send_at) {
+      send_at += n_qt;
+      send_tile(kt, buf);
+    }
     const __bf16* kc = lds + buf * L::kBufElems;
     const __bf16* vc = kc + L::kKElems;
     f32x16 sa[NKB];

@@ -62,6 +62,15 @@ struct FoldParams {
   int32_t P, blk, rem;
   int32_t q_blk[kMaxResident];
   int32_t kv_blk[kMaxResident];
+  // The ring hand-off fused into the fold (bf16 kernel, no mask, resident
+  // blocks all of one length), if send_k is not null: resident r's visiting
+  // block is also written, K to send_k and V to send_v, at element offset
+  // b * send_sb + h * send_sh + send_off[r] + row * d -- the slot the next
+  // ring step reads.  Each tile is written by one workgroup of the resident.
+  void* send_k;
+  void* send_v;
+  int64_t send_sb, send_sh;
+  int64_t send_off[kMaxResident];
 };
 
 // Masking modes (the token layout of the ring when causal).

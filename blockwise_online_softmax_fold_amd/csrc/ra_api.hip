@@ -590,9 +590,17 @@ ra_status_t ring_forward_impl(const void* q, const int64_t q_strides[3], const v
   // the sequence rotated by whole blocks (two copies per batch and tensor).
   bool rotated = n_q == P && bk.rem == 0;
   for (int32_t r = 0; rotated && r < n_q; ++r) rotated = qb(r) == r;
+  // Then, for bf16 without a mask (every workgroup loads every tile of its
+  // visiting block), the fold itself writes the block it visits into the
+  // other slot, at the position of the next resident, which visits that block
+  // at the next step: the ring's send/receive without a separate copy (the
+  // tiles are already in LDS).  Fold t reads slot (t - 1) % 2 (step 0: the
+  // input) and writes slot t % 2, which fold t - 1 read; the stream orders
+  // them.  RA_HANDOFF_COPY=1 keeps the side-stream copies instead.
+  const bool fused = rotated && dt == RA_DTYPE_BF16 && mask == ra::kMaskNone && !env_flag("RA_HANDOFF_COPY");
 
   for (int t = 0; t < P; ++t) {
-    if (t + 1 < P) {
+    if (t + 1 < P && !fused) {
       // Hand-off for step t + 1 (the "send to i+1 / receive from i-1" of
       // step t), issued before step t's fold so the two overlap.
       const int s = slot_of(t + 1);
@@ -626,7 +634,7 @@ ra_status_t ring_forward_impl(const void* q, const int64_t q_strides[3], const v
       }
       if (!serial) RA_HIP(hipEventRecord(dr->ready[s], side), "hipEventRecord");
     }
-    if (t >= 1 && !serial) RA_HIP(hipStreamWaitEvent(stream, dr->ready[slot_of(t)], 0), "hipStreamWaitEvent");
+    if (t >= 1 && !serial && !fused) RA_HIP(hipStreamWaitEvent(stream, dr->ready[slot_of(t)], 0), "hipStreamWaitEvent");
 
     for (int32_t r0 = 0; r0 < n_q; r0 += ra::kMaxResident) {
       const int32_t nr = n_q - r0 < ra::kMaxResident ? n_q - r0 : ra::kMaxResident;
@@ -669,6 +677,14 @@ ra_status_t ring_forward_impl(const void* q, const int64_t q_strides[3], const v
       p.blk = (int32_t)bk.b;
       p.rem = (int32_t)bk.rem;
       p.lse = lse == nullptr ? nullptr : lse + row_of[r0];
+      if (fused && t + 1 < P) {
+        const size_t slot_bytes = (size_t)L.slot_elems * es;
+        p.send_k = kbuf + (size_t)(t & 1) * slot_bytes;
+        p.send_v = vbuf + (size_t)(t & 1) * slot_bytes;
+        p.send_sb = H * L.head_rows * d;
+        p.send_sh = L.head_rows * d;
+        for (int32_t r = 0; r < nr; ++r) p.send_off[r] = (int64_t)((r0 + r + 1) % n_q) * bm * d;
+      }
       p.q_rows = 0;
       for (int32_t r = 0; r < nr; ++r) {
         const int32_t i = qb(r0 + r);
@@ -691,7 +707,8 @@ ra_status_t ring_forward_impl(const void* q, const int64_t q_strides[3], const v
       RA_HIP(ra::launch_fill_u32(vbuf + (size_t)slot_of(t) * slot_bytes, slot_bytes, nan, stream), "poison launch");
     }
     // The slot read by this step is refilled two steps later.
-    if (t >= 1 && t + 2 <= P - 1 && !serial) RA_HIP(hipEventRecord(dr->freed[slot_of(t)], stream), "hipEventRecord");
+    if (t >= 1 && t + 2 <= P - 1 && !serial && !fused)
+      RA_HIP(hipEventRecord(dr->freed[slot_of(t)], stream), "hipEventRecord");
   }
   if (!serial) {
     RA_HIP(hipEventRecord(dr->join, side), "hipEventRecord");

@@ -9,9 +9,10 @@ waits for the transfer before it takes the next block) under stress.
   that does not wait for its copy reads the block of two steps earlier.
 
 Each mode must give the output of the plain run bit for bit, on the rotated
-hand-off (every block resident in ring order: two contiguous copies per
-tensor) and on the block-by-block one (a subset or another order of resident
-blocks, uneven blocks).  The two hand-offs are also compared with each other.
+hand-off (every block resident in ring order: the bf16 fold writes the next
+step's slot itself, other dtypes use two contiguous copies per tensor) and on
+the block-by-block one (a subset or another order of resident blocks, uneven
+blocks).  The hand-offs are also compared with each other.
 """
 
 from __future__ import annotations
@@ -86,6 +87,43 @@ def test_handoff_hazard_modes_are_bitwise_equal(ra, monkeypatch, case, mode):
     # the plain run itself is right
     ref = oracle.ring_attention(to64(q_all), to64(k), to64(v), P, query_blocks=blocks)
     check_output(plain, ref, dt, "plain ring")
+
+
+# (dtype, B, H, N, d, P): every block resident in ring order
+FUSED = [
+    ("bf16", 1, 4, 8192, 128, 8),
+    ("bf16", 1, 2, 8 * 1000, 128, 8),   # ragged last tile (1000 = 15 x 64 + 40)
+    ("bf16", 2, 3, 4 * 100, 128, 4),    # a block shorter than a workgroup's 256 rows
+    ("bf16", 1, 2, 6 * 640, 64, 6),
+    ("bf16", 2, 2, 4096, 256, 4),       # padded LDS rows: duplicated units written twice
+    ("bf16", 1, 1, 66 * 64, 128, 66),   # two launches per step (more than 64 residents)
+]
+
+
+@pytest.mark.parametrize("case", FUSED, ids=[f"{c[0]}-B{c[1]}H{c[2]}N{c[3]}d{c[4]}P{c[5]}" for c in FUSED])
+@pytest.mark.parametrize("mode", ["plain", "poison"])
+def test_fused_hand_off_equals_side_stream_copies(ra, monkeypatch, case, mode):
+    """With every block resident (bf16, no mask) the fold writes the block it
+    visits into the next step's slot itself; RA_HANDOFF_COPY=1 moves it with
+    the side-stream copies instead.  The folds read the same bytes either way,
+    so the outputs are equal bit for bit; with RA_DEBUG_POISON the slot a fold
+    has read is NaN until the next fold overwrites it, so a tile the fused
+    hand-off misses shows up as NaN."""
+    dt, B, H, N, d, P = case
+    _say(f"fused vs copied hand-off ({mode}) {dt} B{B} H{H} N{N} d{d} P{P}")
+    q, k, v = workloads.make_small(B, H, N, d, torch.bfloat16, seed=N + 7 * P + d)
+    if mode == "poison":
+        monkeypatch.setenv("RA_DEBUG_POISON", "1")
+    fused = ra.ra_ring_forward(q, k, v, P)
+    torch.cuda.synchronize()
+    monkeypatch.setenv("RA_HANDOFF_COPY", "1")
+    copied = ra.ra_ring_forward(q, k, v, P)
+    torch.cuda.synchronize()
+    assert torch.isfinite(fused).all(), "a poisoned slot reached the output"
+    assert torch.equal(fused, copied)
+    if mode == "plain":
+        ref = oracle.ring_attention(to64(q), to64(k), to64(v), P)
+        check_output(fused, ref, dt, "fused hand-off ring")
 
 
 def test_poison_is_seen_when_a_slot_is_read_after_it(ra, monkeypatch):
