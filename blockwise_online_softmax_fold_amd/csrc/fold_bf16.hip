@@ -44,6 +44,11 @@
 //  * Workgroup ids are remapped so that consecutive query tiles of one
 //    (batch, head, resident block) -- which read the same K/V -- land on the
 //    same XCD and share its L2.
+//  * The ring's hand-off (math page, "The ring schedule": a device passes the
+//    block it holds on to the next device) can ride on the fold: with
+//    p.send_k set, each workgroup of a resident writes every n_qt-th tile of
+//    the visiting block back out of LDS into the slot the next resident
+//    reads at the next step, so the block moves without being read again.
 //  * Causal masking (math page, "Causal masking, load balance, and other
 //    wrinkles"): positions rise with the row index in every token layout, so
 //    the keys a query tile can see are a prefix of the visiting block.  Tiles

@@ -177,15 +177,20 @@ size_t ra_ring_workspace_bytes(ra_dtype_t dt, int64_t B, int64_t H, int64_t N, i
  * query_blocks: HOST array of n_q block ids in [0, P); NULL means 0..P-1
  *      (then n_q must equal P).
  * On step t resident block i folds block (i - t) mod P.  Step 0 reads the own
- * block in place; the next block is copied into the other half of a per-block
- * double buffer by hipMemcpy2DAsync on a side stream while the current step's
- * fold runs (the stand-in for the ring's send to i+1 / receive from i-1),
- * ordered by events.  When every block is resident in ring order
- * (query_blocks NULL or 0..P-1) and P divides N, the blocks of one step are the
- * sequence rotated by whole blocks, and the hand-off copies it as two
- * contiguous pieces per batch and tensor instead of block by block.
+ * block in place; the next block is moved into the other half of a per-block
+ * double buffer while the current step's fold runs (the stand-in for the
+ * ring's send to i+1 / receive from i-1):
+ *   * every block resident in ring order (query_blocks NULL or 0..P-1), P
+ *     dividing N, bf16: the fold kernel itself writes the block it visits,
+ *     from LDS, to the next resident's place in the other half (stream order
+ *     separates the writer and the readers; environment variable
+ *     RA_HANDOFF_COPY=1 selects the copies below instead);
+ *   * otherwise hipMemcpy2DAsync on a side stream, ordered by events: with
+ *     every block resident in ring order and P dividing N (fp32), the blocks
+ *     of one step are the sequence rotated by whole blocks, copied as two
+ *     contiguous pieces per batch and tensor; else block by block.
  * The (m, l, o) spilled between the ring's steps stays inside the workspace;
- * for bf16 with d = 64 or 128 it is kept relative to a reference maximum at
+ * for bf16 (d = 64, 128, 256) it is kept relative to a reference maximum at
  * most the running maximum (raised lazily) instead of the running maximum
  * itself.  O equals that of the same folds through ra_fold_block followed by
  * ra_finalize up to rounding, not bit for bit.
