@@ -17,13 +17,17 @@ TFLOP/s count only the visible (query, key) pairs, 4 d FLOP each.  With
 --backward one step is one ra_ring_backward (dQ, dK, dV on the same ring; the
 forward that gives O and the log-sum-exp runs once, untimed), counted as the
 five products of the backward, 10 d FLOP per (query, key) pair.  With --graph
-the step is captured once into a HIP graph (stream capture: fold launches,
-hand-off copies, side stream and events all become nodes) and the timed steps
+the step is captured once into a HIP graph (stream capture: fold launches and,
+where the hand-off is copied, the copies, side stream and events all become nodes) and the timed steps
 are graph replays; the fold-launch times in `roofline` then come from eager
 steps.  --device-sweep instead times one device's ring step at its real shape
 (one ra_fold_block of a b-row query block with one b-row visiting block, B1 H32
 d128 bf16) for several b, next to the time one K/V block of that size takes
-over one xGMI link, and prints one JSON line with a row per b.  `clock` is the shader clock the driver reported while the timed steps
+over one xGMI link, and prints one JSON line with a row per b.  `config.handoff`
+says how the ring's K/V hand-off ran: with every block resident in ring order
+(bf16, no mask) the folds write it themselves, and a full run (with the CPU
+baseline) also times the same steps with the side-stream copies
+(RA_HANDOFF_COPY=1) and reports them as `handoff_copy`.  `clock` is the shader clock the driver reported while the timed steps
 ran (sampled from pp_dpm_sclk by a host thread) and the step throughput as a
 share of the peak scaled to that clock (null where the file is not readable);
 `clock.power` is the socket power sampled beside it (hwmon power1_input) with
@@ -523,6 +527,30 @@ def main() -> int:
         ra.ra_profile_folds(False)
     print(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
 
+    # With every block resident in ring order (bf16, no mask) the library's folds
+    # write the ring's hand-off themselves; in a full run (with the CPU baseline:
+    # not the profiling runs, whose kernel counts this would change) the
+    # side-stream copies (RA_HANDOFF_COPY=1), the stand-in the library uses
+    # elsewhere, are timed on the same steps as a second figure.
+    fused = (not args.backward and not args.causal and w.dtype == "bf16" and w.query_blocks is None
+             and w.N % w.P == 0 and not os.environ.get("RA_HANDOFF_COPY"))
+    copy_ms = None
+    if fused and not (args.no_cpu_baseline or args.copy_calibration or args.graph):
+        os.environ["RA_HANDOFF_COPY"] = "1"
+        try:
+            step()
+            torch.cuda.synchronize()
+            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            c0.record()
+            for _ in range(args.steps):
+                step()
+            c1.record()
+            torch.cuda.synchronize()
+            copy_ms = c0.elapsed_time(c1) / args.steps
+        finally:
+            del os.environ["RA_HANDOFF_COPY"]
+        print(f"[bench] same steps with the side-stream copies: {copy_ms:.3f} ms/step", file=sys.stderr, flush=True)
+
     pairs = (w.flops() / (4.0 * w.d)) if not args.causal else _visible_pairs(w, args.causal)
     flops = (10.0 if args.backward else 4.0) * w.d * pairs
     tflops = flops / (ms * 1e-3) / 1e12
@@ -561,12 +589,19 @@ def main() -> int:
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "P": w.P, "b": w.b,
                    "resident_query_blocks": w.n_q, "seed": w.seed, "causal": args.causal or False,
                    "pass": "backward" if args.backward else "forward",
-                   "launch": "hip-graph" if args.graph else "eager"},
+                   "launch": "hip-graph" if args.graph else "eager",
+                   "handoff": ("written by the folds" if fused else
+                               "none (K, V read in place)" if args.backward else "side-stream copies")},
         "pct_mfma_peak": round(100.0 * tflops / peak, 2),
         "exps_per_s": pairs * (2.0 if args.backward else 1.0) / (ms * 1e-3),
         "roofline": roofline,
         "clock": clock.summary(tflops, peak),
     }
+    if copy_ms is not None:
+        rec["handoff_copy"] = {"ms_per_step": round(copy_ms, 4), "value": round(flops / (copy_ms * 1e-3) / 1e12, 2),
+                               "unit": "TFLOP/s", "steps": args.steps,
+                               "note": "the same ring with the hand-off as hipMemcpy2DAsync on a side stream "
+                                       "(RA_HANDOFF_COPY=1), timed after the main steps"}
     if not args.no_cpu_baseline:
         print(f"[bench] timing the CPU oracle for ~{args.cpu_seconds:.0f} s", file=sys.stderr, flush=True)
         # the output rows the oracle computes are checked against the last timed
